@@ -1,0 +1,228 @@
+"""fp64 reference of shared-prefix GQA attention (test infrastructure only).
+
+Sources (page titles; sections as they appear on the pages):
+
+* AHBM Agentic Runtime Architecture, §3.1 -- a branch's page table is the
+  shared prefix pages followed by its private pages; shared pages are
+  referenced, never copied.
+* same page, §1.3 and §3.2 -- combined-Q batching changes the execution
+  shape only; every query row stays independent.
+* ADR-0060 GQA fused attention, §3 (per-tile op sequence) -- scores are
+  Q.K^T times softmax_scale, an additive mask removes invisible keys, then
+  max / exp / sum / P.V.
+* same page, §0.5.3 -- softmax_scale = 1/sqrt(d); the G query heads of one
+  KV head form the query group.
+* same page, §5.4 -- causal visibility of a key tile against a query block.
+* same page, §4 -- the (m, l, O) merge: m = max(m_a, m_b), each side scaled
+  by exp(m_side - m), the output normalised once at the end.
+
+Readings where the pages leave a step open (listed again in the design doc):
+
+* query head h reads KV head floor(h / G) (contiguous groups);
+* the q_len new tokens of a branch are the last q_len positions of its
+  context; key j has position j;
+* causal visibility is inclusive: key position <= query position;
+* private token i of a branch is in page ``page_table[b][i // page_size]``
+  at slot ``i % page_size``;
+* a row that sees no key yields the merge identity (m, l, O) = (-inf, 0, 0);
+  finalising it gives O = 0 and LSE = -inf;
+* LSE = m + ln(l) in scaled-score units (natural log).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+F64 = torch.float64
+EMPTY_LSE = float("-inf")
+
+
+# ---------------------------------------------------------------- indexing --
+def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """KV head read by query head h: the G = H_q / H_kv query heads of one
+    KV head are contiguous (ADR-0060 GQA fused attention, §0.5.3: Q group
+    [G, T_q, d] per KV head)."""
+    return h // (num_q_heads // num_kv_heads)
+
+
+def default_scale(d: int) -> float:
+    """softmax_scale = 1/sqrt(d) (ADR-0060 GQA fused attention, §0.5.3)."""
+    return 1.0 / math.sqrt(d)
+
+
+def lse_of(m: torch.Tensor, l: torch.Tensor) -> torch.Tensor:
+    """Log-sum-exp of a row from its running max and sum: m + ln(l)."""
+    return m + torch.log(l)
+
+
+def query_positions(context_len: int, q_len: int) -> torch.Tensor:
+    """Positions of a branch's new query tokens: the last q_len positions of
+    its context (ADR-0060, §0.5.3 q_block_meta {q_start, T_q}; the new K/V
+    are appended before launch, §0.5.1 precondition P3)."""
+    return torch.arange(context_len - q_len, context_len, dtype=torch.int64)
+
+
+def key_visible(key_pos: torch.Tensor, query_pos: torch.Tensor, causal: bool) -> torch.Tensor:
+    """Boolean [n_query, n_key]: inclusive causal diagonal (ADR-0060, §5.4
+    tile classes); without causality every key of the context is visible
+    (§5.2: decode attends all past KV)."""
+    if not causal:
+        return torch.ones(query_pos.numel(), key_pos.numel(), dtype=torch.bool)
+    return key_pos.view(1, -1) <= query_pos.view(-1, 1)
+
+
+def private_location(i: int, page_size: int) -> Tuple[int, int]:
+    """(logical page, slot) of private token i: tokens are appended to the
+    branch's pages contiguously (AHBM Agentic Runtime Architecture, §3.1;
+    ADR-0060, §2.1)."""
+    return i // page_size, i % page_size
+
+
+# ----------------------------------------------------------------- context --
+def branch_context(inp, b: int, page_size: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K_b, V_b as float64 [C_b, H_kv, d]: the group's shared prefix followed
+    by the branch's private suffix read through its page table
+    (AHBM Agentic Runtime Architecture, §3.1 branch page table)."""
+    g = inp.branch_group[b]
+    s0, sl = inp.group_shared_start[g], inp.group_shared_len[g]
+    ks = inp.k_shared[:, s0:s0 + sl, :].to("cpu", F64).permute(1, 0, 2)
+    vs = inp.v_shared[:, s0:s0 + sl, :].to("cpu", F64).permute(1, 0, 2)
+    n_priv = inp.branch_private_len[b]
+    if n_priv == 0:
+        return ks.contiguous(), vs.contiguous()
+    table = inp.page_table[b].to("cpu").tolist()
+    pages, slots = [], []
+    for i in range(n_priv):
+        lp, slot = private_location(i, page_size)
+        pages.append(table[lp])
+        slots.append(slot)
+    pages_t = torch.tensor(pages, dtype=torch.int64)
+    slots_t = torch.tensor(slots, dtype=torch.int64)
+    kp = inp.k_pages[pages_t.to(inp.k_pages.device), :, slots_t.to(inp.k_pages.device), :]
+    vp = inp.v_pages[pages_t.to(inp.v_pages.device), :, slots_t.to(inp.v_pages.device), :]
+    kp = kp.to("cpu", F64)   # [n_priv, H_kv, d]
+    vp = vp.to("cpu", F64)
+    return torch.cat([ks, kp], 0), torch.cat([vs, vp], 0)
+
+
+def _branch_q_begin(inp) -> List[int]:
+    out, acc = [], 0
+    for t in inp.branch_q_len:
+        out.append(acc)
+        acc += t
+    return out
+
+
+# ---------------------------------------------------------- full attention --
+def _softmax_rows(z: torch.Tensor, v: torch.Tensor):
+    """Full softmax over the last axis of z [..., C] (invisible keys hold
+    -inf) and its product with v [C, d]; returns (O, LSE). Rows with no
+    visible key give O = 0, LSE = -inf."""
+    m = z.max(dim=-1, keepdim=True).values
+    empty = torch.isinf(m) & (m < 0)
+    m_safe = torch.where(empty, torch.zeros_like(m), m)
+    p = torch.exp(z - m_safe)                      # exp(-inf) = 0 for masked keys
+    l = p.sum(dim=-1, keepdim=True)
+    o = (p @ v) / torch.where(empty, torch.ones_like(l), l)
+    lse = torch.where(empty, torch.full_like(m, EMPTY_LSE), lse_of(m, l))
+    return o, lse.squeeze(-1)
+
+
+def attention(inp, num_kv_heads: int, page_size: int, causal: bool,
+              softmax_scale: Optional[float] = None,
+              tokens: Optional[Sequence[int]] = None,
+              heads: Optional[Sequence[int]] = None,
+              max_block: int = 1 << 22):
+    """O [n_tok, H_q, d] and LSE [n_tok, H_q] in float64.
+
+    ``tokens`` (global query-token indices) and ``heads`` restrict the
+    computation to a sample; the returned tensors then have shape
+    [len(tokens), len(heads), d] and [len(tokens), len(heads)].
+    """
+    n_tok, H_q, d = inp.q.shape
+    scale = default_scale(d) if softmax_scale is None else softmax_scale
+    q_begin = _branch_q_begin(inp)
+    tok_list = list(range(n_tok)) if tokens is None else list(tokens)
+    head_list = list(range(H_q)) if heads is None else list(heads)
+    out_o = torch.zeros(len(tok_list), len(head_list), d, dtype=F64)
+    out_l = torch.full((len(tok_list), len(head_list)), EMPTY_LSE, dtype=F64)
+    where = {t: i for i, t in enumerate(tok_list)}
+    for b in range(len(inp.branch_q_len)):
+        T = inp.branch_q_len[b]
+        if T == 0:
+            continue
+        mine = [t for t in range(q_begin[b], q_begin[b] + T) if t in where]
+        if not mine:
+            continue
+        kb, vb = branch_context(inp, b, page_size)
+        C = kb.shape[0]
+        qpos_all = query_positions(C, T)
+        kpos = torch.arange(C, dtype=torch.int64)
+        chunk = max(1, max_block // max(1, C))
+        for c0 in range(0, len(mine), chunk):
+            toks = mine[c0:c0 + chunk]
+            local = torch.tensor([t - q_begin[b] for t in toks], dtype=torch.int64)
+            qrows = inp.q[torch.tensor(toks, device=inp.q.device)].to("cpu", F64)   # [n, H_q, d]
+            vis = key_visible(kpos, qpos_all[local], causal)                       # [n, C]
+            for hi, h in enumerate(head_list):
+                kv = kv_head_of(h, H_q, num_kv_heads)
+                z = scale * (qrows[:, h, :] @ kb[:, kv, :].T)                     # [n, C]
+                z = z.masked_fill(~vis, float("-inf"))
+                o, lse = _softmax_rows(z, vb[:, kv, :])
+                rows = torch.tensor([where[t] for t in toks])
+                out_o[rows, hi] = o
+                out_l[rows, hi] = lse
+    return out_o, out_l
+
+
+# ------------------------------------------------------ partials and merge --
+def partial_state(q_rows: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  key_pos: torch.Tensor, row_pos: torch.Tensor, causal: bool,
+                  softmax_scale: float):
+    """Unnormalised online-softmax state (m, l, O) of rows q_rows [R, d]
+    over one shard of keys k, v [N, d] (AHBM Agentic Runtime Architecture,
+    §3.3 per-PE local attention; ADR-0060, §3 running state). A row that
+    sees none of the shard's keys gets the identity (-inf, 0, 0)."""
+    q_rows, k, v = q_rows.to(F64), k.to(F64), v.to(F64)
+    R, d = q_rows.shape
+    if k.shape[0] == 0:
+        return (torch.full((R,), float("-inf"), dtype=F64), torch.zeros(R, dtype=F64),
+                torch.zeros(R, d, dtype=F64))
+    z = softmax_scale * (q_rows @ k.T)
+    vis = key_visible(key_pos, row_pos, causal)
+    z = z.masked_fill(~vis, float("-inf"))
+    m = z.max(dim=-1).values
+    empty = torch.isinf(m) & (m < 0)
+    m_safe = torch.where(empty, torch.zeros_like(m), m)
+    p = torch.exp(z - m_safe.unsqueeze(-1))
+    return m, p.sum(-1), p @ v
+
+
+def merge_states(a, b):
+    """Log-sum-exp merge of two (m, l, O) states (ADR-0060 GQA fused
+    attention, §4): m = max(m_a, m_b); each side is scaled by
+    exp(m_side - m). exp(-inf - (-inf)) is taken as 0, so the identity
+    (-inf, 0, 0) merges away (a reading: the pages leave that case open)."""
+    ma, la, oa = a
+    mb, lb, ob = b
+    m = torch.maximum(ma, mb)
+    both_empty = torch.isinf(m) & (m < 0)
+    m_safe = torch.where(both_empty, torch.zeros_like(m), m)
+    sa = torch.exp(ma - m_safe)
+    sb = torch.exp(mb - m_safe)
+    return m, la * sa + lb * sb, oa * sa.unsqueeze(-1) + ob * sb.unsqueeze(-1)
+
+
+def finalize(state):
+    """O = O / l once at the end, LSE = m + ln(l) (ADR-0060, §4: normalise
+    once at the root; §0.5.4: N = 1 stores O / l directly)."""
+    m, l, o = state
+    empty = l == 0
+    o_n = o / torch.where(empty, torch.ones_like(l), l).unsqueeze(-1)
+    o_n = torch.where(empty.unsqueeze(-1), torch.zeros_like(o_n), o_n)
+    lse = torch.where(empty, torch.full_like(m, EMPTY_LSE),
+                      lse_of(m, torch.where(empty, torch.ones_like(l), l)))
+    return o_n, lse

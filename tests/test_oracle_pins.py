@@ -1,0 +1,65 @@
+"""The fp64 oracle against its pins, and planted mistakes against the pins.
+
+Every pin must pass on the oracle as written. Then each plausible mistake
+(a wrong index, a dropped term, a swapped operand) is planted in the oracle
+on the CPU, and at least one pin must catch it -- otherwise the pins would
+not be able to tell a wrong oracle from a right one.
+"""
+
+import math
+
+import pytest
+import torch
+
+import oracle
+from oracle import fp64 as OA
+
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin()
+
+
+def _merge_drop_b_scale(a, b):
+    ma, la, oa = a
+    mb, lb, ob = b
+    m = torch.maximum(ma, mb)
+    sa = torch.exp(ma - m)
+    return m, la * sa + lb, oa * sa.unsqueeze(-1) + ob
+
+
+def _branch_context_swapped(inp, b, page_size):
+    k, v = ORIGINAL_BRANCH_CONTEXT(inp, b, page_size)
+    return v, k
+
+
+ORIGINAL_BRANCH_CONTEXT = OA.branch_context
+
+MUTATIONS = {
+    "gqa_interleaved_heads": ("kv_head_of", lambda h, hq, hkv: h % hkv),
+    "queries_at_first_positions": ("query_positions", lambda C, T: torch.arange(0, T)),
+    "causal_strict_diagonal": ("key_visible",
+                               lambda kp, qp, c: (kp.view(1, -1) < qp.view(-1, 1)) if c
+                               else torch.ones(qp.numel(), kp.numel(), dtype=torch.bool)),
+    "causal_ignored": ("key_visible",
+                       lambda kp, qp, c: torch.ones(qp.numel(), kp.numel(), dtype=torch.bool)),
+    "page_and_slot_swapped": ("private_location", lambda i, ps: (i % ps, i // ps)),
+    "slot_off_by_one": ("private_location", lambda i, ps: (i // ps, (i + 1) % ps)),
+    "scale_dropped": ("default_scale", lambda d: 1.0),
+    "scale_one_over_d": ("default_scale", lambda d: 1.0 / d),
+    "lse_without_max": ("lse_of", lambda m, l: torch.log(l)),
+    "lse_log2": ("lse_of", lambda m, l: m + torch.log2(l)),
+    "merge_drops_rescale": ("merge_states", _merge_drop_b_scale),
+    "k_and_v_swapped": ("branch_context", _branch_context_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    failing = P.failing_pins()
+    assert failing, f"planted mistake {name!r} passed every pin"

@@ -1,0 +1,10 @@
+"""Seeded synthetic workloads for shared-prefix GQA attention.
+
+This package holds only shapes, seeds and random-number draws. It contains
+none of the attention arithmetic, so both the CPU oracle (``oracle/``) and
+the HIP path (``gqa_attention_agentic_amd``) can take their inputs from it
+without sharing any code of the method.
+"""
+
+from .configs import Workload, CONFIGS, get_config, custom, Branch, Group  # noqa: F401
+from .generate import generate, Inputs  # noqa: F401
