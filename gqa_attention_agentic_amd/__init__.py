@@ -1,0 +1,154 @@
+"""MI355X (gfx950) shared-prefix GQA flash attention.
+
+Python face of ``libgqa_attn.so`` (C ABI in ``include/gqa_attn.h``). The
+functions here marshal torch tensors and Python lists into the C calls;
+PyTorch only provides device memory and the stream. Every step of the
+attention -- the Q fold, paged K/V reads, QK^T and PV on MFMA, the online
+softmax, causal tile skipping and the log-sum-exp merge -- runs in the
+library's HIP kernels. If the library is missing, ``load()`` raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import GqaError, load  # noqa: F401
+
+__all__ = ["GqaAttention", "plan_host", "load", "GqaError"]
+
+_DTYPES = {"bf16": _lib.GQA_BF16, "fp32": _lib.GQA_FP32}
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in (torch.bfloat16, "bf16"):
+        return _lib.GQA_BF16
+    if dtype in (torch.float32, "fp32"):
+        return _lib.GQA_FP32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _check_lengths(ng, nb, group_shared_len, branch_q_len, branch_private_len, splits):
+    """The C ABI takes bare host pointers; their lengths are checked here."""
+    if len(group_shared_len) != ng:
+        raise ValueError("group_shared_len must have one entry per group")
+    if len(branch_q_len) != nb or len(branch_private_len) != nb:
+        raise ValueError("branch arrays must have one entry per branch")
+    if splits is not None and len(splits) != ng + nb:
+        raise ValueError("splits_override must have n_groups + n_branches entries")
+
+
+class GqaAttention:
+    """One handle: fixed head geometry, page size and dtype; reusable across
+    forwards (the plan is rebuilt only when the metadata changes)."""
+
+    def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                 dtype="bf16", softmax_scale: float = 0.0, workspace_bytes_cap: int = 0):
+        self.lib = load()
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.page_size = page_size
+        self.dtype_code = _dtype_code(dtype)
+        p = _lib.params(num_q_heads, num_kv_heads, head_dim, page_size, self.dtype_code,
+                        softmax_scale, workspace_bytes_cap)
+        h = ctypes.c_void_p()
+        _lib.check(self.lib.gqa_attn_create(ctypes.byref(p), ctypes.byref(h)))
+        self._h = h
+        self._n_units = 0
+
+    # ------------------------------------------------------------ forward --
+    def forward(self, q, k_shared, v_shared, k_pages, v_pages, page_table,
+                group_shared_start: Sequence[int], group_shared_len: Sequence[int],
+                branch_group: Sequence[int], branch_q_len: Sequence[int],
+                branch_private_len: Sequence[int], causal: bool,
+                splits: Optional[Sequence[int]] = None, out=None, lse=None, stream=None):
+        import torch
+        dev = q.device
+        want = torch.bfloat16 if self.dtype_code == _lib.GQA_BF16 else torch.float32
+        for name, t in (("q", q), ("k_shared", k_shared), ("v_shared", v_shared),
+                        ("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.dtype != want or t.device != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor on {dev}")
+        if page_table.dtype != torch.int32 or page_table.device != dev or not page_table.is_contiguous():
+            raise ValueError("page_table must be a contiguous int32 tensor on the same device")
+        n_tok = q.shape[0]
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(n_tok, self.num_q_heads, dtype=torch.float32, device=dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        ng, nb = len(group_shared_start), len(branch_group)
+        _check_lengths(ng, nb, group_shared_len, branch_q_len, branch_private_len, splits)
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() > 0 else 0)
+        st = self.lib.gqa_attn_forward(
+            self._h, ptr(q), ptr(k_shared), ptr(v_shared), ptr(k_pages), ptr(v_pages), ptr(page_table),
+            int(page_table.shape[1]) if page_table.dim() == 2 else 0,
+            ng, _lib.int_array(group_shared_start), _lib.int_array(group_shared_len),
+            nb, _lib.int_array(branch_group), _lib.int_array(branch_q_len),
+            _lib.int_array(branch_private_len), _lib.int_array(splits), int(bool(causal)),
+            ptr(out), ptr(lse), ctypes.c_void_p(stream))
+        _lib.check(st)
+        self._n_units = ng + nb
+        return out, lse
+
+    def forward_inputs(self, inp, causal: bool, splits=None, out=None, lse=None, stream=None):
+        """forward() on a ``workload.Inputs`` record."""
+        return self.forward(inp.q, inp.k_shared, inp.v_shared, inp.k_pages, inp.v_pages, inp.page_table,
+                            inp.group_shared_start, inp.group_shared_len, inp.branch_group,
+                            inp.branch_q_len, inp.branch_private_len, causal, splits=splits,
+                            out=out, lse=lse, stream=stream)
+
+    # ------------------------------------------------------- introspection --
+    def plan_stats(self) -> dict:
+        s = _lib.PlanStats()
+        _lib.check(self.lib.gqa_attn_plan_stats(self._h, ctypes.byref(s)))
+        return s.as_dict()
+
+    def plan_splits(self):
+        arr = (ctypes.c_int32 * max(1, self._n_units))()
+        _lib.check(self.lib.gqa_attn_plan_splits(self._h, arr, self._n_units))
+        return list(arr)[: self._n_units]
+
+    def enable_timing(self, on: bool = True) -> None:
+        _lib.check(self.lib.gqa_attn_enable_timing(self._h, int(bool(on))))
+
+    def kernel_times(self):
+        """(attention ms, merge ms, forwards) summed since timing was enabled."""
+        a, m, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+        _lib.check(self.lib.gqa_attn_kernel_times(self._h, ctypes.byref(a), ctypes.byref(m), ctypes.byref(n)))
+        return a.value, m.value, n.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self.lib.gqa_attn_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def plan_host(num_q_heads, num_kv_heads, head_dim, page_size, group_shared_start, group_shared_len,
+              branch_group, branch_q_len, branch_private_len, causal, splits=None, dtype="bf16"):
+    """Host-only planner (no device use): returns (items, splits, stats) where
+    items is a list of (unit_slot, kv, row_begin, n_rows, key_begin, key_end,
+    split, kernel) tuples; kernel 0 = 128-row, 1 = 32-row."""
+    lib = load()
+    p = _lib.params(num_q_heads, num_kv_heads, head_dim, page_size, _dtype_code(dtype))
+    ng, nb = len(group_shared_start), len(branch_group)
+    _check_lengths(ng, nb, group_shared_len, branch_q_len, branch_private_len, splits)
+    args = (ctypes.byref(p), ng, _lib.int_array(group_shared_start), _lib.int_array(group_shared_len),
+            nb, _lib.int_array(branch_group), _lib.int_array(branch_q_len),
+            _lib.int_array(branch_private_len), _lib.int_array(splits), int(bool(causal)))
+    n = ctypes.c_int64()
+    _lib.check(lib.gqa_attn_plan_host(*args, None, 0, ctypes.byref(n), None, None))
+    items = (ctypes.c_int32 * max(8, 8 * n.value))()
+    spl = (ctypes.c_int32 * max(1, ng + nb))()
+    stats = _lib.PlanStats()
+    _lib.check(lib.gqa_attn_plan_host(*args, items, n.value, ctypes.byref(n), spl, ctypes.byref(stats)))
+    flat = list(items)
+    return ([tuple(flat[8 * i:8 * i + 8]) for i in range(n.value)], list(spl)[: ng + nb], stats.as_dict())

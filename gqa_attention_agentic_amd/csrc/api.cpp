@@ -1,0 +1,452 @@
+// C ABI of the shared-prefix GQA attention library (declared in gqa_attn.h).
+//
+// A forward call validates its arguments on the host, builds (or reuses) the
+// plan, copies it to the device through pinned staging with one async copy,
+// and launches up to three kernels on the caller's stream: the 128-row
+// attention kernel, the 32-row attention kernel and the LSE merge. It never
+// synchronises the stream; the only allocations happen when the plan or the
+// partial workspace outgrows what the handle already holds.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gqa_attn.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gqa_status fail(gqa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+gqa_status hip_fail(hipError_t e, const char* what) {
+  return fail(GQA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct TimerSlot {
+  hipEvent_t ev[4];   // attention start, attention end, merge start, merge end
+  bool merged;
+};
+
+}  // namespace
+
+struct gqa_attn {
+  gqa_attn_params p{};
+  int device = 0;
+  int n_cu = 256;
+  // plan cache
+  std::vector<int32_t> key;
+  gqa::Plan plan;
+  bool have_plan = false;
+  // device plan buffer and its pinned staging
+  char* d_plan = nullptr;
+  size_t d_plan_cap = 0;
+  char* h_staging = nullptr;
+  size_t h_staging_cap = 0;
+  hipEvent_t staging_free = nullptr;   // recorded after the last staging -> device copy
+  size_t off_wide = 0, off_narrow = 0, off_units = 0, off_branches = 0, off_tiles = 0;
+  // partial workspace
+  char* d_work = nullptr;
+  size_t d_work_cap = 0;
+  // timing
+  bool timing = false;
+  std::vector<TimerSlot> timers;
+  size_t timers_used = 0;
+};
+
+namespace {
+
+gqa_status check_params(const gqa_attn_params* p) {
+  if (!p) return fail(GQA_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(GQA_ERR_INVALID_ARG, "num_q_heads and num_kv_heads must be > 0");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(GQA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(GQA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (p->page_size <= 0 || p->page_size > 4096)
+    return fail(GQA_ERR_INVALID_ARG, "page_size must be in 1..4096");
+  if (p->dtype != GQA_BF16 && p->dtype != GQA_FP32) return fail(GQA_ERR_INVALID_ARG, "unknown dtype");
+  if (p->workspace_bytes_cap < 0) return fail(GQA_ERR_INVALID_ARG, "workspace_bytes_cap < 0");
+  if (!(std::isfinite(p->softmax_scale))) return fail(GQA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  return GQA_OK;
+}
+
+gqa_status make_input(const gqa_attn_params* p, int32_t n_groups, const int32_t* gs, const int32_t* gl,
+                      int32_t n_branches, const int32_t* bg, const int32_t* bq, const int32_t* bp,
+                      const int32_t* splits, int32_t causal, int n_cu, gqa::PlanInput* in) {
+  if (n_groups < 0 || n_branches < 0) return fail(GQA_ERR_INVALID_ARG, "negative group or branch count");
+  if (n_groups > 0 && (!gs || !gl)) return fail(GQA_ERR_INVALID_ARG, "group arrays are NULL");
+  if (n_branches > 0 && (!bg || !bq || !bp)) return fail(GQA_ERR_INVALID_ARG, "branch arrays are NULL");
+  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  in->H_q = p->num_q_heads;
+  in->H_kv = p->num_kv_heads;
+  in->D = p->head_dim;
+  in->page_size = p->page_size;
+  in->dtype = p->dtype;
+  in->causal = causal;
+  in->n_cu = n_cu;
+  in->g_start.assign(gs, gs + n_groups);
+  in->g_len.assign(gl, gl + n_groups);
+  in->b_group.assign(bg, bg + n_branches);
+  in->b_qlen.assign(bq, bq + n_branches);
+  in->b_priv.assign(bp, bp + n_branches);
+  if (splits) in->splits_override.assign(splits, splits + n_groups + n_branches);
+  std::string err = gqa::validate_plan_input(*in);
+  if (!err.empty()) return fail(GQA_ERR_INVALID_ARG, err);
+  return GQA_OK;
+}
+
+void fill_stats(const gqa::Plan& P, int64_t D, gqa_plan_stats* s) {
+  s->n_items_wide = (int64_t)P.wide.size();
+  s->n_items_narrow = (int64_t)P.narrow.size();
+  s->n_kv_tiles = P.n_kv_tiles;
+  s->n_merge_rows = P.merge_rows;
+  s->workspace_bytes = P.part_rows * (D + 2) * (int64_t)sizeof(float);
+  s->n_units = (int64_t)P.units.size();
+  s->max_splits = P.max_splits;
+  s->reserved = 0;
+}
+
+// Serialised plan: wide items | narrow items | units | branches | tiles.
+size_t plan_layout(gqa_attn* h) {
+  const gqa::Plan& P = h->plan;
+  size_t off = 0;
+  h->off_wide = off;
+  off = align_up(off + P.wide.size() * sizeof(gqa::WorkItem), 256);
+  h->off_narrow = off;
+  off = align_up(off + P.narrow.size() * sizeof(gqa::WorkItem), 256);
+  h->off_units = off;
+  off = align_up(off + P.units.size() * sizeof(gqa::UnitDesc), 256);
+  h->off_branches = off;
+  off = align_up(off + P.branches.size() * sizeof(gqa::BranchDesc), 256);
+  h->off_tiles = off;
+  off = align_up(off + P.tiles.size() * sizeof(gqa::TileInfo), 256);
+  return std::max<size_t>(off, 256);
+}
+
+gqa_status upload_plan(gqa_attn* h, hipStream_t stream) {
+  const size_t bytes = plan_layout(h);
+  hipError_t e;
+  // The staging buffer may still feed the previous copy.
+  if (h->staging_free) {
+    e = hipEventSynchronize(h->staging_free);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  if (bytes > h->h_staging_cap) {
+    if (h->h_staging) hipHostFree(h->h_staging);
+    h->h_staging = nullptr;
+    h->h_staging_cap = 0;
+    e = hipHostMalloc((void**)&h->h_staging, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "pinned plan staging allocation failed");
+    h->h_staging_cap = bytes;
+  }
+  if (bytes > h->d_plan_cap) {
+    if (h->d_plan) {
+      e = hipFree(h->d_plan);   // synchronises the device: no kernel still reads it
+      if (e != hipSuccess) return hip_fail(e, "hipFree(plan)");
+    }
+    h->d_plan = nullptr;
+    h->d_plan_cap = 0;
+    e = hipMalloc((void**)&h->d_plan, bytes);
+    if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "device plan allocation failed");
+    h->d_plan_cap = bytes;
+  }
+  const gqa::Plan& P = h->plan;
+  auto put = [&](size_t off, const void* src, size_t n) {
+    if (n) std::memcpy(h->h_staging + off, src, n);
+  };
+  put(h->off_wide, P.wide.data(), P.wide.size() * sizeof(gqa::WorkItem));
+  put(h->off_narrow, P.narrow.data(), P.narrow.size() * sizeof(gqa::WorkItem));
+  put(h->off_units, P.units.data(), P.units.size() * sizeof(gqa::UnitDesc));
+  put(h->off_branches, P.branches.data(), P.branches.size() * sizeof(gqa::BranchDesc));
+  put(h->off_tiles, P.tiles.data(), P.tiles.size() * sizeof(gqa::TileInfo));
+  e = hipMemcpyAsync(h->d_plan, h->h_staging, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  if (!h->staging_free) {
+    e = hipEventCreateWithFlags(&h->staging_free, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  e = hipEventRecord(h->staging_free, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return GQA_OK;
+}
+
+gqa_status ensure_workspace(gqa_attn* h) {
+  const size_t rows = (size_t)h->plan.part_rows;
+  const size_t need = rows ? align_up(rows * sizeof(float2), 256) + rows * (size_t)h->p.head_dim * sizeof(float) : 0;
+  if (h->p.workspace_bytes_cap > 0 && need > (size_t)h->p.workspace_bytes_cap)
+    return fail(GQA_ERR_NO_MEMORY, "partial workspace of " + std::to_string(need) +
+                                       " bytes exceeds workspace_bytes_cap");
+  if (need <= h->d_work_cap) return GQA_OK;
+  hipError_t e;
+  if (h->d_work) {
+    e = hipFree(h->d_work);
+    if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+  }
+  h->d_work = nullptr;
+  h->d_work_cap = 0;
+  e = hipMalloc((void**)&h->d_work, need);
+  if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "workspace allocation of " + std::to_string(need) + " bytes failed");
+  h->d_work_cap = need;
+  return GQA_OK;
+}
+
+TimerSlot* next_timer(gqa_attn* h) {
+  if (h->timers_used == h->timers.size()) {
+    TimerSlot t{};
+    for (auto& ev : t.ev)
+      if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    h->timers.push_back(t);
+  }
+  return &h->timers[h->timers_used++];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_attn_last_error(void) { return g_last_error.c_str(); }
+
+gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out) {
+  if (!out) return fail(GQA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  gqa_status s = check_params(p);
+  if (s != GQA_OK) return s;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int ncu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  gqa_attn* h = new gqa_attn();
+  h->p = *p;
+  if (h->p.softmax_scale <= 0.f) h->p.softmax_scale = 1.0f / std::sqrt((float)p->head_dim);
+  h->device = dev;
+  h->n_cu = ncu > 0 ? ncu : 256;
+  *out = h;
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_destroy(gqa_attn* h) {
+  if (!h) return GQA_OK;
+  hipSetDevice(h->device);
+  hipDeviceSynchronize();
+  if (h->d_plan) hipFree(h->d_plan);
+  if (h->d_work) hipFree(h->d_work);
+  if (h->h_staging) hipHostFree(h->h_staging);
+  if (h->staging_free) hipEventDestroy(h->staging_free);
+  for (auto& t : h->timers)
+    for (auto& ev : t.ev) hipEventDestroy(ev);
+  delete h;
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, const void* v_shared,
+                            const void* k_pages, const void* v_pages, const int32_t* page_table,
+                            int32_t max_pages_per_branch, int32_t n_groups,
+                            const int32_t* group_shared_start, const int32_t* group_shared_len,
+                            int32_t n_branches, const int32_t* branch_group, const int32_t* branch_q_len,
+                            const int32_t* branch_private_len, const int32_t* splits_override,
+                            int32_t causal, void* o, float* lse, void* stream) {
+  if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  gqa::PlanInput in;
+  gqa_status s = make_input(&h->p, n_groups, group_shared_start, group_shared_len, n_branches,
+                            branch_group, branch_q_len, branch_private_len, splits_override, causal,
+                            h->n_cu, &in);
+  if (s != GQA_OK) return s;
+
+  // Plan cache key: every input of the planner.
+  std::vector<int32_t> key;
+  key.reserve(8 + 2 * n_groups + 4 * n_branches);
+  key.push_back(n_groups);
+  key.push_back(n_branches);
+  key.push_back(causal);
+  key.push_back(splits_override ? 1 : 0);
+  key.insert(key.end(), in.g_start.begin(), in.g_start.end());
+  key.insert(key.end(), in.g_len.begin(), in.g_len.end());
+  key.insert(key.end(), in.b_group.begin(), in.b_group.end());
+  key.insert(key.end(), in.b_qlen.begin(), in.b_qlen.end());
+  key.insert(key.end(), in.b_priv.begin(), in.b_priv.end());
+  key.insert(key.end(), in.splits_override.begin(), in.splits_override.end());
+  const bool same = h->have_plan && key == h->key;
+  gqa::Plan fresh;
+  const gqa::Plan& P = same ? h->plan : fresh;
+  if (!same) {
+    std::string err = gqa::build_plan(in, &fresh);
+    if (!err.empty()) return fail(GQA_ERR_INVALID_ARG, err);
+  }
+
+  // Pointer checks against the (new) plan's extents.
+  const bool any_q = P.n_q_tokens > 0;
+  bool any_priv = false;
+  for (int32_t b = 0; b < n_branches; ++b) any_priv |= in.b_priv[b] > 0;
+  if (any_q && (!q || !o || !lse)) return fail(GQA_ERR_INVALID_ARG, "q, o and lse must be non-NULL");
+  if (P.n_shared_tokens > 0 && (!k_shared || !v_shared))
+    return fail(GQA_ERR_INVALID_ARG, "k_shared and v_shared must be non-NULL");
+  if (any_priv && (!k_pages || !v_pages || !page_table))
+    return fail(GQA_ERR_INVALID_ARG, "k_pages, v_pages and page_table must be non-NULL");
+  if (any_priv && max_pages_per_branch < P.max_branch_pages)
+    return fail(GQA_ERR_INVALID_ARG, "max_pages_per_branch is smaller than a branch's page count");
+  const void* ptrs[] = {q, k_shared, v_shared, k_pages, v_pages, page_table, o, lse};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (!any_q) return GQA_OK;
+
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  if (!same) {
+    h->plan = std::move(fresh);
+    h->key = std::move(key);
+    h->have_plan = true;
+    s = upload_plan(h, st);
+    if (s != GQA_OK) {
+      h->have_plan = false;
+      return s;
+    }
+  }
+  s = ensure_workspace(h);
+  if (s != GQA_OK) return s;
+
+  const gqa::Plan& Q = h->plan;
+  gqa::AttnArgs a{};
+  a.q = q;
+  a.k_shared = k_shared;
+  a.v_shared = v_shared;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.page_table = page_table;
+  a.units = (const gqa::UnitDesc*)(h->d_plan + h->off_units);
+  a.branches = (const gqa::BranchDesc*)(h->d_plan + h->off_branches);
+  a.tiles = (const gqa::TileInfo*)(h->d_plan + h->off_tiles);
+  a.part_ml = (float2*)h->d_work;
+  a.part_o = (float*)(h->d_work + align_up((size_t)Q.part_rows * sizeof(float2), 256));
+  a.o = o;
+  a.lse = lse;
+  a.max_pages = max_pages_per_branch;
+  a.n_branches = n_branches;
+  a.H_q = h->p.num_q_heads;
+  a.H_kv = h->p.num_kv_heads;
+  a.G = a.H_q / a.H_kv;
+  a.n_shared = Q.n_shared_tokens;
+  a.page_size = h->p.page_size;
+  a.page_shift = -1;
+  for (int sft = 0; sft < 13; ++sft)
+    if ((1 << sft) == h->p.page_size) a.page_shift = sft;
+  a.causal = causal;
+  a.n_q_tokens = Q.n_q_tokens;
+  a.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
+
+  TimerSlot* tm = h->timing ? next_timer(h) : nullptr;
+  if (tm) hipEventRecord(tm->ev[0], st);
+  if (!Q.wide.empty()) {
+    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
+    e = gqa::launch_attention(a, (int32_t)Q.wide.size(), false, h->p.dtype, h->p.head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
+  }
+  if (!Q.narrow.empty()) {
+    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
+    e = gqa::launch_attention(a, (int32_t)Q.narrow.size(), true, h->p.dtype, h->p.head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
+  }
+  if (tm) hipEventRecord(tm->ev[1], st);
+  if (tm) tm->merged = Q.merge_rows > 0;
+  if (Q.merge_rows > 0) {
+    if (tm) hipEventRecord(tm->ev[2], st);
+    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    if (tm) hipEventRecord(tm->ev[3], st);
+  }
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_plan_stats(const gqa_attn* h, gqa_plan_stats* out) {
+  if (!h || !out) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  if (!h->have_plan) return fail(GQA_ERR_INVALID_ARG, "no forward has been planned on this handle");
+  fill_stats(h->plan, h->p.head_dim, out);
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n) {
+  if (!h || !out) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  if (!h->have_plan) return fail(GQA_ERR_INVALID_ARG, "no forward has been planned on this handle");
+  if (n != (int32_t)h->plan.api_splits.size())
+    return fail(GQA_ERR_INVALID_ARG, "n must equal n_groups + n_branches of the last forward");
+  std::memcpy(out, h->plan.api_splits.data(), sizeof(int32_t) * n);
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable) {
+  if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  h->timing = enable != 0;
+  h->timers_used = 0;
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms, int64_t* n_forwards) {
+  if (!h || !attn_ms || !merge_ms || !n_forwards) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  double at = 0.0, mg = 0.0;
+  for (size_t k = 0; k < h->timers_used; ++k) {
+    TimerSlot& t = h->timers[k];
+    hipError_t e = hipEventSynchronize(t.merged ? t.ev[3] : t.ev[1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.ev[0], t.ev[1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    at += ms;
+    if (t.merged) {
+      e = hipEventElapsedTime(&ms, t.ev[2], t.ev[3]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      mg += ms;
+    }
+  }
+  *attn_ms = at;
+  *merge_ms = mg;
+  *n_forwards = (int64_t)h->timers_used;
+  h->timers_used = 0;
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_plan_host(const gqa_attn_params* p, int32_t n_groups, const int32_t* group_shared_start,
+                              const int32_t* group_shared_len, int32_t n_branches, const int32_t* branch_group,
+                              const int32_t* branch_q_len, const int32_t* branch_private_len,
+                              const int32_t* splits_override, int32_t causal, int32_t* items, int64_t cap,
+                              int64_t* n_items, int32_t* splits, gqa_plan_stats* stats) {
+  gqa_status s = check_params(p);
+  if (s != GQA_OK) return s;
+  gqa::PlanInput in;
+  s = make_input(p, n_groups, group_shared_start, group_shared_len, n_branches, branch_group, branch_q_len,
+                 branch_private_len, splits_override, causal, 256, &in);
+  if (s != GQA_OK) return s;
+  gqa::Plan P;
+  std::string err = gqa::build_plan(in, &P);
+  if (!err.empty()) return fail(GQA_ERR_INVALID_ARG, err);
+  const int64_t n = (int64_t)(P.wide.size() + P.narrow.size());
+  if (n_items) *n_items = n;
+  if (items && cap >= n) {
+    int64_t k = 0;
+    for (int pass = 0; pass < 2; ++pass)
+      for (const gqa::WorkItem& w : (pass == 0 ? P.wide : P.narrow)) {
+        int32_t* r = items + 8 * k++;
+        r[0] = P.unit_slot[w.unit]; r[1] = w.kv; r[2] = w.row_begin; r[3] = w.n_rows;
+        r[4] = w.key_begin; r[5] = w.key_end; r[6] = w.split; r[7] = pass;
+      }
+  }
+  if (splits) std::memcpy(splits, P.api_splits.data(), sizeof(int32_t) * P.api_splits.size());
+  if (stats) fill_stats(P, p->head_dim, stats);
+  return GQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,640 @@
+// Split-KV GQA flash attention for gfx950 (CDNA4), bf16 or fp32.
+//
+// Per work item (unit, KV head, M-tile, KV shard) a workgroup of 4 waves
+// runs the FlashAttention tile loop of ADR-0060 GQA fused attention (TL;DR
+// kernel and §3 per-tile op sequence) on the rows of its M-tile:
+//
+//   S^T = K Q^T * scale      v_mfma_f32_32x32x16_bf16 (fp32: 32x32x2_f32)
+//   mask                     only in tiles that cross the causal diagonal or
+//                            the ragged end of the shard (§5.4 tile classes)
+//   m' = max(m, rowmax S^T)  online softmax in fp32, log2 domain
+//   P  = exp2(S^T - m'), l = l * 2^(m-m') + rowsum P
+//   O^T = O^T * 2^(m-m') + V^T P^T
+//
+// Rows are (query token, g) pairs: the G query heads of a KV head and the
+// tokens of every branch that shares the KV range are one M dimension
+// (ADR-0060, §5.2; AHBM Agentic Runtime Architecture, §1.3 and §3.2), so a
+// K/V tile read once into LDS serves all of them.
+//
+// Layout choices for CDNA4:
+//  * S is computed transposed (keys x rows). In the 32x32 MFMA output a lane
+//    then holds one row and 16 keys of it, so the row max / row sum are
+//    in-lane plus a single exchange between the two half-waves, and the
+//    rescale of O^T by 2^(m-m') is one scalar per lane.
+//  * The S^T registers are already the B operand of V^T P^T (the contraction
+//    index order is free as long as both operands agree), so P never leaves
+//    registers.
+//  * V is transposed while it is staged into LDS (V^T rows of BN keys, keys
+//    permuted inside each 16-key chunk so that one 16-byte LDS read yields a
+//    lane's 8 operand values). K stays [key][d] with a padded pitch.
+//  * Wide kernel (MFMA-bound fan-out / prefill): 128 rows, 4 waves x 32 rows,
+//    64-key K/V^T tiles double-buffered in LDS, the next tile's global loads
+//    in flight while the current one is computed.
+//  * Narrow kernel (KV-bandwidth-bound decode, <= 32 rows): every wave
+//    streams its own 32-key tiles with the next one prefetched in registers;
+//    the 4 per-wave (m, l, O) states are merged through LDS at the end.
+//  * A row with exactly one live partial in total writes O / l and LSE
+//    directly (ADR-0060, §0.5.4 N = 1); otherwise the unnormalised partial
+//    (m, l, O) goes to the workspace for the merge kernel (§4).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Branch that owns query token `tok`: the last branch in [lo, hi) whose
+// first token is <= tok (branches with no tokens share their successor's
+// q_begin and are never returned for a real token).
+__device__ __forceinline__ int branch_of(const BranchDesc* br, int lo, int hi, int tok) {
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (br[mid].q_begin <= tok) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Live partial count of unit `ui` for row (tok, g) and the workspace row of
+// its shard 0 for KV head kv (shard s is at base + s * bm).
+__device__ __forceinline__ int unit_live(const AttnArgs& a, int ui, int tok, int g, int kv,
+                                         int64_t* base) {
+  const UnitDesc& u = a.units[ui];
+  const int r = (tok - u.tok_begin) * a.G + g;
+  const int t = r / u.bm;
+  const TileInfo ti = a.tiles[u.tile_off + t];
+  *base = ti.part_off + ((int64_t)kv * ti.live) * u.bm + (r - t * u.bm);
+  return ti.live;
+}
+
+template <typename T, int D, bool NARROW>
+struct Cfg {
+  static constexpr bool BF16 = std::is_same<T, uint16_t>::value;
+  static constexpr int BN = NARROW ? kNarrowKeys : kWideKeys;   // keys per tile
+  static constexpr int BM = NARROW ? kNarrowRows : kWideRows;   // rows per item
+  static constexpr int LOADERS = NARROW ? 64 : 256;             // threads loading one tile
+  static constexpr int VEC = 16 / (int)sizeof(T);               // elements per 16-byte chunk
+  static constexpr int CHUNKS = BN * D / VEC;                   // chunks per tensor per tile
+  static constexpr int CPT = CHUNKS / LOADERS;                  // chunks per thread per tensor
+  static constexpr int KP = BF16 ? D + 8 : D + 1;               // K row pitch (elements)
+  static constexpr int VP = BF16 ? BN + 8 : D + 4;              // V^T (bf16) / V (fp32) pitch
+  static constexpr int K_ELEMS = BN * KP;
+  static constexpr int V_ELEMS = BF16 ? D * VP : BN * VP;
+  static constexpr int STAGE = ((K_ELEMS + V_ELEMS) * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int NSTAGE = NARROW ? 4 : 2;
+  static constexpr int OB = D / 32;                             // O^T blocks per lane
+  static constexpr int SB = BN / 32;                            // S^T blocks per tile
+  static constexpr int QF = BF16 ? D / 16 : D / 2;              // Q fragments per lane
+  static constexpr int MERGE = NARROW ? 4 * (OB * 16 * 64 + 2 * 64) * 4 : 0;
+  static constexpr int LDS = (STAGE * NSTAGE > MERGE) ? STAGE * NSTAGE : MERGE;
+  static_assert(CHUNKS % LOADERS == 0, "tile does not split evenly over the loaders");
+  static_assert(!BF16 || CPT == 2 || CPT % 4 == 0, "V transpose needs 2 or a multiple of 4 keys per thread");
+  static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU exceeded");
+};
+
+template <class C>
+struct Stage {
+  uint4 k[C::CPT];
+  uint4 v[C::CPT];
+};
+
+template <class C>
+struct State {
+  typename std::conditional<C::BF16, bf16x8_t, float>::type qf[C::QF];
+  f32x16_t o[C::OB];
+  float m;   // running max, log2 units
+  float l;   // running sum
+};
+
+template <int D>
+__device__ __forceinline__ int64_t kv_offset(const AttnArgs& a, const UnitDesc& u, int kv, int key) {
+  if (u.kind == kShared) return ((int64_t)kv * a.n_shared + u.src + key) * D;
+  int lp, slot;
+  if (a.page_shift >= 0) {
+    lp = key >> a.page_shift;
+    slot = key & (a.page_size - 1);
+  } else {
+    lp = key / a.page_size;
+    slot = key - lp * a.page_size;
+  }
+  const int page = a.page_table[(int64_t)u.src * a.max_pages + lp];
+  return (((int64_t)page * a.H_kv + kv) * a.page_size + slot) * D;
+}
+
+// Global -> registers for the KV tile whose first unit-local key is key0.
+// Keys at or past key_end are not read (the ragged tail is zero-filled).
+template <class C, typename T, int D>
+__device__ __forceinline__ void load_tile(const AttnArgs& a, const UnitDesc& u, int kv, int key0,
+                                          int key_end, int ltid, Stage<C>& st) {
+  const T* kb = (const T*)(u.kind == kShared ? a.k_shared : a.k_pages);
+  const T* vb = (const T*)(u.kind == kShared ? a.v_shared : a.v_pages);
+  constexpr int CPR = D / C::VEC;   // chunks per key row
+#pragma unroll
+  for (int j = 0; j < C::CPT; ++j) {
+    const int c = ltid + C::LOADERS * j;
+    const int key = key0 + c / CPR;
+    const int col = (c % CPR) * C::VEC;
+    if (key < key_end) {
+      const int64_t off = kv_offset<D>(a, u, kv, key) + col;
+      st.k[j] = *(const uint4*)(kb + off);
+      if (!C::BF16) st.v[j] = *(const uint4*)(vb + off);
+    } else {
+      st.k[j] = make_uint4(0, 0, 0, 0);
+      if (!C::BF16) st.v[j] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  if (C::BF16) {
+    // V: each thread takes CPT consecutive keys of one 8-wide d slice, so
+    // that it can write them transposed.
+    constexpr int KG = C::BN / C::CPT;
+    const int kg = ltid % KG, oct = ltid / KG;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int key = key0 + kg * C::CPT + i;
+      if (key < key_end) st.v[i] = *(const uint4*)(vb + kv_offset<D>(a, u, kv, key) + oct * 8);
+      else st.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Position of key k inside its 16-key chunk in the V^T LDS rows: bits 2 and
+// 3 swapped, so that a lane's 8 P.V operand keys are 8 consecutive slots.
+__device__ __forceinline__ int vt_slot(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <class C, typename T, int D>
+__device__ __forceinline__ void store_tile(T* Ks, T* Vs, int ltid, const Stage<C>& st) {
+  constexpr int CPR = D / C::VEC;
+#pragma unroll
+  for (int j = 0; j < C::CPT; ++j) {
+    const int c = ltid + C::LOADERS * j;
+    const int key = c / CPR;
+    const int col = (c % CPR) * C::VEC;
+    if (C::BF16) {
+      *(uint4*)(Ks + key * C::KP + col) = st.k[j];
+    } else {
+      float* kd = (float*)Ks + key * C::KP + col;
+      kd[0] = __uint_as_float(st.k[j].x);
+      kd[1] = __uint_as_float(st.k[j].y);
+      kd[2] = __uint_as_float(st.k[j].z);
+      kd[3] = __uint_as_float(st.k[j].w);
+      *(uint4*)((float*)Vs + key * C::VP + col) = st.v[j];
+    }
+  }
+  if (C::BF16) {
+    constexpr int KG = C::BN / C::CPT;
+    const int kg = ltid % KG, oct = ltid / KG;
+    uint16_t* vt = (uint16_t*)Vs;
+#pragma unroll
+    for (int di = 0; di < 8; ++di) {
+      uint16_t* row = vt + (oct * 8 + di) * C::VP;
+      const int sh = (di & 1) * 16;
+#define GQA_HALF(i) ((((const uint32_t*)&st.v[i])[di >> 1] >> sh) & 0xffffu)
+      if (C::CPT == 2) {
+        const int k0 = kg * 2;
+        const int slot = (k0 & ~15) | vt_slot(k0 & 15);
+        *(uint32_t*)(row + slot) = GQA_HALF(0) | (GQA_HALF(1) << 16);
+      } else {
+#pragma unroll
+        for (int run = 0; run < C::CPT / 4; ++run) {
+          const int k0 = kg * C::CPT + run * 4;
+          const int slot = (k0 & ~15) | vt_slot(k0 & 15);
+          uint2 w;
+          w.x = GQA_HALF(run * 4 + 0) | (GQA_HALF(run * 4 + 1) << 16);
+          w.y = GQA_HALF(run * 4 + 2) | (GQA_HALF(run * 4 + 3) << 16);
+          *(uint2*)(row + slot) = w;
+        }
+      }
+#undef GQA_HALF
+    }
+  }
+}
+
+// One KV tile for one wave's 32 rows: S^T, mask, online softmax, O^T += V^T P^T.
+template <class C, typename T, int D>
+__device__ __forceinline__ void compute_tile(const T* Ks, const T* Vs, State<C>& s, int tile_key0,
+                                             int n_valid, bool need_mask, int causal, int key_pos0,
+                                             int row_pos, float scale_log2, int i, int h) {
+  f32x16_t sacc[C::SB];
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+    if constexpr (C::BF16) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8_t av = *(const bf16x8_t*)(Ks + (32 * kb + i) * C::KP + 16 * ks + 8 * h);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s.qf[ks], sacc[kb], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 2; ++ks) {
+        const float av = ((const float*)Ks)[(32 * kb + i) * C::KP + 2 * ks + h];
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, s.qf[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+  }
+  // scale into log2 units, mask, row max
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = sacc[kb][r] * scale_log2;
+      if (need_mask) {
+        const int kl = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool vis = kl < n_valid && (!causal || key_pos0 + tile_key0 + kl <= row_pos);
+        v = vis ? v : kNegInf;
+      }
+      sacc[kb][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(s.m, mx);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  const float corr = exp2_fast(s.m - m_use);
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(sacc[kb][r] - m_use);
+      sacc[kb][r] = p;
+      rs += p;
+    }
+  }
+  rs += __shfl_xor(rs, 32);
+  s.l = s.l * corr + rs;
+  s.m = m_new;
+#pragma unroll
+  for (int db = 0; db < C::OB; ++db) s.o[db] *= corr;
+
+  if constexpr (C::BF16) {
+#pragma unroll
+    for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * c + e];
+#pragma unroll
+        for (int db = 0; db < C::OB; ++db) {
+          const bf16x8_t av =
+              *(const bf16x8_t*)(Vs + (32 * db + i) * C::VP + (2 * kb + c) * 16 + 8 * h);
+          s.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, s.o[db], 0, 0, 0);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+        for (int db = 0; db < C::OB; ++db) {
+          const float av = ((const float*)Vs)[key * C::VP + 32 * db + i];
+          s.o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sacc[kb][r], s.o[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Per-lane row bookkeeping.
+struct Row {
+  int tok, g, b, pos;
+  bool ok;
+};
+
+__device__ __forceinline__ Row row_of(const AttnArgs& a, const UnitDesc& u, int r, bool ok) {
+  Row w;
+  w.ok = ok;
+  w.tok = u.tok_begin + r / a.G;
+  w.g = r - (r / a.G) * a.G;
+  w.b = u.branch_lo;
+  w.pos = -1;
+  if (ok) {
+    w.b = (u.kind == kShared) ? branch_of(a.branches, u.branch_lo, u.branch_hi, w.tok) : u.src;
+    const BranchDesc br = a.branches[w.b];
+    w.pos = br.ctx_len - br.q_len + (w.tok - br.q_begin);
+  }
+  return w;
+}
+
+template <class C, typename T, int D>
+__device__ __forceinline__ void load_q(const AttnArgs& a, const Row& w, int kv, int h, State<C>& s) {
+  const T* q = (const T*)a.q + ((int64_t)w.tok * a.H_q + kv * a.G + w.g) * D;
+#pragma unroll
+  for (int f = 0; f < C::QF; ++f) {
+    if constexpr (C::BF16) {
+      uint4 x = w.ok ? *(const uint4*)(q + 16 * f + 8 * h) : make_uint4(0, 0, 0, 0);
+      s.qf[f] = __builtin_bit_cast(bf16x8_t, x);
+    } else {
+      s.qf[f] = w.ok ? ((const float*)q)[2 * f + h] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < C::OB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s.o[db][r] = 0.f;
+  s.m = kNegInf;
+  s.l = 0.f;
+}
+
+// Final or partial write of one lane's row for O^T blocks [db0, db1).
+template <class C, typename T, int D>
+__device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it, const UnitDesc& u,
+                                          const Row& w, float m, float l, const f32x16_t* o,
+                                          int db0, int db1, bool write_scalars, int h) {
+  if (!w.ok) return;
+  int64_t base_own, base_oth;
+  const int live_own = unit_live(a, it.unit, w.tok, w.g, it.kv, &base_own);
+  const BranchDesc br = a.branches[w.b];
+  const int oth = (u.kind == kShared) ? br.unit_pr : br.unit_sh;
+  const int live_oth = (oth >= 0) ? unit_live(a, oth, w.tok, w.g, it.kv, &base_oth) : 0;
+  (void)live_own;
+  if (live_own + live_oth == 1) {
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const int64_t orow = ((int64_t)w.tok * a.H_q + it.kv * a.G + w.g) * D;
+    for (int db = db0; db < db1; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * h;
+        const float x0 = o[db - db0][4 * q4 + 0] * inv, x1 = o[db - db0][4 * q4 + 1] * inv;
+        const float x2 = o[db - db0][4 * q4 + 2] * inv, x3 = o[db - db0][4 * q4 + 3] * inv;
+        if constexpr (C::BF16) {
+          uint2 pk;
+          pk.x = pack_bf16x2(x0, x1);
+          pk.y = pack_bf16x2(x2, x3);
+          *(uint2*)((uint16_t*)a.o + orow + d0) = pk;
+        } else {
+          *(float4*)((float*)a.o + orow + d0) = make_float4(x0, x1, x2, x3);
+        }
+      }
+    }
+    if (write_scalars && h == 0)
+      a.lse[(int64_t)w.tok * a.H_q + it.kv * a.G + w.g] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : kNegInf;
+  } else {
+    const int64_t prow = base_own + (int64_t)it.split * u.bm;
+    float* po = a.part_o + prow * D;
+    for (int db = db0; db < db1; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * h;
+        *(float4*)(po + d0) = make_float4(o[db - db0][4 * q4 + 0], o[db - db0][4 * q4 + 1],
+                                          o[db - db0][4 * q4 + 2], o[db - db0][4 * q4 + 3]);
+      }
+    }
+    if (write_scalars && h == 0) a.part_ml[prow] = make_float2(m, l);
+  }
+}
+
+// Smallest / largest valid row position of the wave.
+__device__ __forceinline__ void wave_pos_range(const Row& w, int* pmin, int* pmax) {
+  int lo = w.ok ? w.pos : 0x7fffffff, hi = w.ok ? w.pos : -1;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) {
+    lo = min(lo, __shfl_xor(lo, x));
+    hi = max(hi, __shfl_xor(hi, x));
+  }
+  *pmin = lo;
+  *pmax = hi;
+}
+
+// ---------------------------------------------------------------- wide ----
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+attn_wide(AttnArgs a) {
+  using C = Cfg<T, D, false>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  const WorkItem it = a.items[blockIdx.x];
+  const UnitDesc u = a.units[it.unit];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
+  const int rloc = wave * 32 + i;
+  const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
+  State<C> s;
+  load_q<C, T, D>(a, w, it.kv, h, s);
+  int pmin, pmax;
+  wave_pos_range(w, &pmin, &pmax);
+  const bool wave_rows = wave * 32 < it.n_rows;
+
+  const int nkeys = it.key_end - it.key_begin;
+  const int nt = (nkeys + C::BN - 1) / C::BN;
+  Stage<C> st;
+  load_tile<C, T, D>(a, u, it.kv, it.key_begin, it.key_end, tid, st);
+  store_tile<C, T, D>((T*)smem, (T*)(smem + C::K_ELEMS * sizeof(T)), tid, st);
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const bool more = j + 1 < nt;
+    if (more) load_tile<C, T, D>(a, u, it.kv, it.key_begin + (j + 1) * C::BN, it.key_end, tid, st);
+    const int tk0 = it.key_begin + j * C::BN;                  // unit-local first key of the tile
+    const int nvalid = min(C::BN, it.key_end - tk0);
+    const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
+    if (wave_rows && !future) {
+      const bool need_mask = (nvalid < C::BN) || (a.causal && u.key_pos0 + tk0 + C::BN - 1 > pmin);
+      char* stg = smem + (j & 1) * C::STAGE;
+      compute_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, tk0, nvalid,
+                            need_mask, a.causal, u.key_pos0, w.pos, a.scale_log2, i, h);
+    }
+    if (more) {
+      char* stg = smem + ((j + 1) & 1) * C::STAGE;
+      store_tile<C, T, D>((T*)stg, (T*)(stg + C::K_ELEMS * sizeof(T)), tid, st);
+    }
+    __syncthreads();
+  }
+  write_row<C, T, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
+}
+
+// -------------------------------------------------------------- narrow ----
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+attn_narrow(AttnArgs a) {
+  using C = Cfg<T, D, true>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  const WorkItem it = a.items[blockIdx.x];
+  const UnitDesc u = a.units[it.unit];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
+  const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+  State<C> s;
+  load_q<C, T, D>(a, w, it.kv, h, s);
+  int pmin, pmax;
+  wave_pos_range(w, &pmin, &pmax);
+
+  const int nkeys = it.key_end - it.key_begin;
+  const int nt = (nkeys + C::BN - 1) / C::BN;   // wave tiles; wave w takes w, w+4, ...
+  const int rounds = (nt + 3) / 4;
+  char* stg = smem + wave * C::STAGE;
+  T* Ks = (T*)stg;
+  T* Vs = (T*)(stg + C::K_ELEMS * sizeof(T));
+  Stage<C> st;
+  if (wave < nt) load_tile<C, T, D>(a, u, it.kv, it.key_begin + wave * C::BN, it.key_end, lane, st);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int j = wave + 4 * rd;
+    const bool have = j < nt;
+    if (have) store_tile<C, T, D>(Ks, Vs, lane, st);
+    __syncthreads();
+    if (j + 4 < nt) load_tile<C, T, D>(a, u, it.kv, it.key_begin + (j + 4) * C::BN, it.key_end, lane, st);
+    if (have) {
+      const int tk0 = it.key_begin + j * C::BN;
+      const int nvalid = min(C::BN, it.key_end - tk0);
+      const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
+      if (!future) {
+        const bool need_mask = (nvalid < C::BN) || (a.causal && u.key_pos0 + tk0 + C::BN - 1 > pmin);
+        compute_tile<C, T, D>(Ks, Vs, s, tk0, nvalid, need_mask, a.causal, u.key_pos0, w.pos,
+                              a.scale_log2, i, h);
+      }
+    }
+    __syncthreads();
+  }
+  // Merge the four waves' states (same rows, disjoint keys) through LDS.
+  float* mo = (float*)smem;                       // [wave][db][r][lane]
+  float2* mml = (float2*)(smem + 4 * C::OB * 16 * 64 * 4);
+#pragma unroll
+  for (int db = 0; db < C::OB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
+  mml[wave * 64 + lane] = make_float2(s.m, s.l);
+  __syncthreads();
+  float mk[4], lk[4];
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 x = mml[k * 64 + lane];
+    mk[k] = x.x;
+    lk[k] = x.y;
+    M = fmaxf(M, x.x);
+  }
+  const float M_use = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, wk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    wk[k] = exp2_fast(mk[k] - M_use);
+    L += lk[k] * wk[k];
+  }
+  for (int db = wave; db < C::OB; db += 4) {
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
+      acc[r] = x;
+    }
+    write_row<C, T, D>(a, it, u, w, M, L, &acc, db, db + 1, wave == 0, h);
+  }
+}
+
+// --------------------------------------------------------------- merge ----
+// One workgroup per (query token, KV head); each thread owns 4 consecutive
+// d values of one of the G rows. Partials are combined in a fixed order
+// (prefix shards, then suffix shards), so the result is bitwise repeatable
+// (ADR-0060 GQA fused attention, §4: m = max m_i, weights exp(m_i - m),
+// normalise once at the end).
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+lse_merge(AttnArgs a) {
+  const int tok = blockIdx.x / a.H_kv, kv = blockIdx.x - tok * a.H_kv;
+  constexpr int TPR = D / 4;   // threads per row
+  const int b = branch_of(a.branches, 0, a.n_branches, tok);
+  const BranchDesc br = a.branches[b];
+  for (int g = threadIdx.x / TPR; g < a.G; g += 256 / TPR) {
+    const int d0 = (threadIdx.x % TPR) * 4;
+    int64_t base[2] = {0, 0};
+    int live[2] = {0, 0}, bm[2] = {0, 0};
+    if (br.unit_sh >= 0) {
+      live[0] = unit_live(a, br.unit_sh, tok, g, kv, &base[0]);
+      bm[0] = a.units[br.unit_sh].bm;
+    }
+    if (br.unit_pr >= 0) {
+      live[1] = unit_live(a, br.unit_pr, tok, g, kv, &base[1]);
+      bm[1] = a.units[br.unit_pr].bm;
+    }
+    if (live[0] + live[1] < 2) continue;   // written directly by the attention kernel
+    float M = kNegInf;
+    for (int x = 0; x < 2; ++x)
+      for (int sI = 0; sI < live[x]; ++sI) M = fmaxf(M, a.part_ml[base[x] + (int64_t)sI * bm[x]].x);
+    const float M_use = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int x = 0; x < 2; ++x)
+      for (int sI = 0; sI < live[x]; ++sI) {
+        const int64_t p = base[x] + (int64_t)sI * bm[x];
+        const float2 ml = a.part_ml[p];
+        const float wgt = exp2_fast(ml.x - M_use);
+        L += ml.y * wgt;
+        const float4 v = *(const float4*)(a.part_o + p * D + d0);
+        o0 += wgt * v.x;
+        o1 += wgt * v.y;
+        o2 += wgt * v.z;
+        o3 += wgt * v.w;
+      }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    const int64_t orow = ((int64_t)tok * a.H_q + kv * a.G + g);
+    if constexpr (std::is_same<T, uint16_t>::value) {
+      uint2 pk;
+      pk.x = pack_bf16x2(o0 * inv, o1 * inv);
+      pk.y = pack_bf16x2(o2 * inv, o3 * inv);
+      *(uint2*)((uint16_t*)a.o + orow * D + d0) = pk;
+    } else {
+      *(float4*)((float*)a.o + orow * D + d0) = make_float4(o0 * inv, o1 * inv, o2 * inv, o3 * inv);
+    }
+    if (d0 == 0) a.lse[orow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStream_t st) {
+  if (n_items <= 0) return hipSuccess;
+  if (narrow) hipLaunchKernelGGL((attn_narrow<T, D>), dim3(n_items), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_wide<T, D>), dim3(n_items), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_merge_t(const AttnArgs& a, hipStream_t st) {
+  const int64_t blocks = (int64_t)a.n_q_tokens * a.H_kv;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((lse_merge<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int dtype, int head_dim,
+                            hipStream_t stream) {
+  if (dtype == 0) {
+    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, n_items, narrow, stream);
+    return launch_attn_t<uint16_t, 64>(a, n_items, narrow, stream);
+  }
+  if (head_dim == 128) return launch_attn_t<float, 128>(a, n_items, narrow, stream);
+  return launch_attn_t<float, 64>(a, n_items, narrow, stream);
+}
+
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  if (dtype == 0) {
+    if (head_dim == 128) return launch_merge_t<uint16_t, 128>(a, stream);
+    return launch_merge_t<uint16_t, 64>(a, stream);
+  }
+  if (head_dim == 128) return launch_merge_t<float, 128>(a, stream);
+  return launch_merge_t<float, 64>(a, stream);
+}
+
+}  // namespace gqa

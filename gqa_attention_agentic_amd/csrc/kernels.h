@@ -1,0 +1,46 @@
+// Launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan_types.h"
+
+namespace gqa {
+
+struct AttnArgs {
+  const void* q;
+  const void* k_shared;
+  const void* v_shared;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* page_table;
+  const WorkItem* items;
+  const UnitDesc* units;
+  const BranchDesc* branches;
+  const TileInfo* tiles;
+  float* part_o;        // [part_rows, D] unnormalised partial O
+  float2* part_ml;      // [part_rows] (m in log2 units, l)
+  void* o;              // [n_q_tokens, H_q, D] storage dtype
+  float* lse;           // [n_q_tokens, H_q]
+  int32_t max_pages;
+  int32_t n_branches;
+  int32_t H_q;
+  int32_t H_kv;
+  int32_t G;
+  int32_t n_shared;     // tokens per KV head in k_shared / v_shared
+  int32_t page_size;
+  int32_t page_shift;   // log2(page_size) when a power of two, else -1
+  int32_t causal;
+  int32_t n_q_tokens;
+  float scale_log2;     // softmax_scale * log2(e)
+  int32_t pad;
+};
+
+// Attention over a work-item list. narrow selects the 32-row kernel.
+hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int dtype,
+                            int head_dim, hipStream_t stream);
+
+// Log-sum-exp merge of the partials of every output row with >= 2 of them.
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,342 @@
+// Host planner for shared-prefix GQA attention (see plan.h).
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <functional>
+#include <limits>
+#include <queue>
+
+namespace gqa {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, f, a, b, c);
+  return buf;
+}
+
+// Shard boundaries of a key range of length L into S shards. Long shards are
+// aligned to the kernel's KV tile so that only the last tile of a unit is
+// ragged; short ones are cut evenly (shard boundaries are not observable in
+// the result: ADR-0060 GQA fused attention, §4 -- the merge is associative
+// and commutative).
+std::vector<int32_t> shard_bounds(int32_t L, int32_t S, int32_t tile) {
+  std::vector<int32_t> b;
+  if (L <= 0) return b;
+  S = std::max(1, std::min(S, L));
+  b.push_back(0);
+  const bool align = (int64_t)L >= (int64_t)S * 2 * tile;
+  for (int32_t s = 1; s < S; ++s) {
+    int64_t x = (int64_t)s * L / S;
+    if (align) x = std::min<int64_t>(L, ceil_div(x, tile) * tile);
+    if (x > b.back() && x < L) b.push_back((int32_t)x);
+  }
+  b.push_back(L);
+  return b;
+}
+
+struct UnitWork {
+  int32_t unit;
+  std::vector<int32_t> tile_key_end;   // causal clamp per M-tile (unit-local keys)
+};
+
+// Makespan of a list of item costs on `slots` identical workers, largest
+// first (list scheduling in the order the kernel's grid is issued).
+double lpt_makespan(std::vector<double> cost, int slots) {
+  std::sort(cost.begin(), cost.end(), std::greater<double>());
+  std::priority_queue<double, std::vector<double>, std::greater<double>> heap;
+  for (int i = 0; i < slots; ++i) heap.push(0.0);
+  double mk = 0.0;
+  for (double c : cost) {
+    double t = heap.top() + c;
+    heap.pop();
+    heap.push(t);
+    mk = std::max(mk, t);
+  }
+  return mk;
+}
+
+}  // namespace
+
+std::string validate_plan_input(const PlanInput& in) {
+  if (in.H_q <= 0 || in.H_kv <= 0) return "num_q_heads and num_kv_heads must be > 0";
+  if (in.H_q % in.H_kv != 0) return "num_q_heads must be a multiple of num_kv_heads";
+  if (in.D != 64 && in.D != 128) return "head_dim must be 64 or 128";
+  if (in.page_size <= 0 || in.page_size > 4096) return "page_size must be in 1..4096";
+  const size_t ng = in.g_start.size(), nb = in.b_group.size();
+  if (in.g_len.size() != ng) return "group arrays differ in length";
+  if (in.b_qlen.size() != nb || in.b_priv.size() != nb) return "branch arrays differ in length";
+  if (!in.splits_override.empty() && in.splits_override.size() != ng + nb)
+    return "splits_override must have n_groups + n_branches entries";
+  int64_t q_total = 0;
+  for (size_t g = 0; g < ng; ++g) {
+    if (in.g_start[g] < 0 || in.g_len[g] < 0) return fmt("group %lld: negative start or length", (long long)g);
+  }
+  int32_t last_group = -1;
+  std::vector<char> closed(ng, 0);
+  for (size_t b = 0; b < nb; ++b) {
+    const int32_t g = in.b_group[b];
+    if (g < 0 || (size_t)g >= ng) return fmt("branch %lld: group %lld out of range", (long long)b, g);
+    if (in.b_qlen[b] < 0 || in.b_priv[b] < 0) return fmt("branch %lld: negative length", (long long)b);
+    if ((int64_t)in.b_qlen[b] > (int64_t)in.g_len[g] + in.b_priv[b])
+      return fmt("branch %lld: q_len %lld exceeds its context", (long long)b, in.b_qlen[b]);
+    if (g != last_group) {
+      if (closed[g]) return fmt("branches of group %lld are not consecutive", g);
+      if (last_group >= 0) closed[last_group] = 1;
+      last_group = g;
+    }
+    q_total += in.b_qlen[b];
+  }
+  if (q_total > (int64_t)std::numeric_limits<int32_t>::max() / in.H_q)
+    return "too many query rows";
+  for (int32_t s : in.splits_override)
+    if (s < 0 || s > 4096) return "splits_override entries must be in 0..4096";
+  return "";
+}
+
+std::string build_plan(const PlanInput& in, Plan* P) {
+  std::string err = validate_plan_input(in);
+  if (!err.empty()) return err;
+  *P = Plan();
+  const int32_t G = in.H_q / in.H_kv;
+  const int32_t ng = (int32_t)in.g_start.size(), nb = (int32_t)in.b_group.size();
+
+  // Branches: token ranges and context lengths; per-token positions (host only).
+  P->branches.resize(nb);
+  std::vector<int32_t> pos_of_tok;
+  int32_t q_acc = 0;
+  for (int32_t b = 0; b < nb; ++b) {
+    BranchDesc& d = P->branches[b];
+    d.q_begin = q_acc;
+    d.q_len = in.b_qlen[b];
+    d.ctx_len = in.g_len[in.b_group[b]] + in.b_priv[b];
+    d.unit_sh = d.unit_pr = -1;
+    d.group = in.b_group[b];
+    d.pad0 = d.pad1 = 0;
+    for (int32_t t = 0; t < d.q_len; ++t) pos_of_tok.push_back(d.ctx_len - d.q_len + t);
+    q_acc += d.q_len;
+    P->max_branch_pages = std::max<int32_t>(P->max_branch_pages,
+                                            (int32_t)ceil_div(in.b_priv[b], in.page_size));
+  }
+  P->n_q_tokens = q_acc;
+  for (int32_t g = 0; g < ng; ++g)
+    P->n_shared_tokens = std::max(P->n_shared_tokens, in.g_start[g] + in.g_len[g]);
+
+  // Units: each group's prefix (rows = all its branches' tokens), then each
+  // branch's private suffix.
+  std::vector<int32_t> api_slot;   // unit -> index in the API's split list
+  for (int32_t g = 0; g < ng; ++g) {
+    int32_t lo = -1, hi = -1, ntok = 0;
+    for (int32_t b = 0; b < nb; ++b)
+      if (in.b_group[b] == g) {
+        if (lo < 0) lo = b;
+        hi = b + 1;
+        ntok += in.b_qlen[b];
+      }
+    if (lo < 0 || ntok == 0 || in.g_len[g] == 0) continue;
+    UnitDesc u{};
+    u.kind = kShared;
+    u.tok_begin = P->branches[lo].q_begin;
+    u.n_tok = ntok;
+    u.src = in.g_start[g];
+    u.key_len = in.g_len[g];
+    u.key_pos0 = 0;
+    u.branch_lo = lo;
+    u.branch_hi = hi;
+    for (int32_t b = lo; b < hi; ++b) P->branches[b].unit_sh = (int32_t)P->units.size();
+    api_slot.push_back(g);
+    P->units.push_back(u);
+  }
+  for (int32_t b = 0; b < nb; ++b) {
+    if (in.b_priv[b] == 0 || in.b_qlen[b] == 0) continue;
+    UnitDesc u{};
+    u.kind = kPrivate;
+    u.tok_begin = P->branches[b].q_begin;
+    u.n_tok = in.b_qlen[b];
+    u.src = b;
+    u.key_len = in.b_priv[b];
+    u.key_pos0 = in.g_len[in.b_group[b]];
+    u.branch_lo = b;
+    u.branch_hi = b + 1;
+    P->branches[b].unit_pr = (int32_t)P->units.size();
+    api_slot.push_back(ng + b);
+    P->units.push_back(u);
+  }
+
+  // M-tiles and their causal key clamp.
+  const int32_t nu = (int32_t)P->units.size();
+  std::vector<UnitWork> uw(nu);
+  for (int32_t ui = 0; ui < nu; ++ui) {
+    UnitDesc& u = P->units[ui];
+    const int64_t M = (int64_t)u.n_tok * G;
+    u.bm = (M <= kNarrowRows) ? kNarrowRows : kWideRows;
+    const int32_t ntile = (int32_t)ceil_div(M, u.bm);
+    uw[ui].unit = ui;
+    uw[ui].tile_key_end.resize(ntile);
+    for (int32_t t = 0; t < ntile; ++t) {
+      const int64_t r0 = (int64_t)t * u.bm, r1 = std::min<int64_t>(M, r0 + u.bm);
+      int32_t pmax = -1;
+      for (int64_t tok = u.tok_begin + r0 / G; tok <= u.tok_begin + (r1 - 1) / G; ++tok)
+        pmax = std::max(pmax, pos_of_tok[tok]);
+      int64_t kend = u.key_len;
+      if (in.causal) kend = std::min<int64_t>(u.key_len, std::max<int64_t>(0, (int64_t)pmax - u.key_pos0 + 1));
+      uw[ui].tile_key_end[t] = (int32_t)kend;
+    }
+  }
+
+  // Split counts: the caller's override, else the heuristic below.
+  std::vector<int32_t> S(nu, 0);
+  auto override_of = [&](int32_t ui) -> int32_t {
+    return in.splits_override.empty() ? 0 : in.splits_override[api_slot[ui]];
+  };
+  // KV-bandwidth-bound units (<= 32 rows, decode-like): cut the total KV
+  // stream into about one item per resident workgroup slot, no shard below
+  // 256 keys, so every slot streams a similar number of bytes (ADR-0060,
+  // §5.2-§5.3: decode is bound by KV loads).
+  const int64_t slots = 2LL * in.n_cu;
+  {
+    int64_t wn = 0;
+    for (int32_t ui = 0; ui < nu; ++ui)
+      if (P->units[ui].bm == kNarrowRows && override_of(ui) == 0) wn += (int64_t)in.H_kv * P->units[ui].key_len;
+    const int64_t chunk = std::max<int64_t>(256, ceil_div(wn, slots));
+    for (int32_t ui = 0; ui < nu; ++ui)
+      if (P->units[ui].bm == kNarrowRows && override_of(ui) == 0)
+        S[ui] = (int32_t)std::max<int64_t>(1, ceil_div(P->units[ui].key_len, chunk));
+  }
+  // MFMA-bound units (fan-out, prefill): choose one shard length for all of
+  // them by estimating the makespan of the resulting items on the resident
+  // slots (largest first) plus the cost of writing and merging partials --
+  // the runtime cost model of AHBM Agentic Runtime Architecture, §4.5 in
+  // one-GPU form: more shards fill more compute units but add merge traffic.
+  {
+    std::vector<int32_t> wide_auto;
+    int32_t maxlen = 0;
+    for (int32_t ui = 0; ui < nu; ++ui)
+      if (P->units[ui].bm == kWideRows && override_of(ui) == 0) {
+        wide_auto.push_back(ui);
+        maxlen = std::max(maxlen, P->units[ui].key_len);
+      }
+    if (!wide_auto.empty()) {
+      // Cost units: one key of one item (the time a wave spends on one key
+      // with 32 rows); fixed per-item cost ~ 96 keys; a partial row costs
+      // its bytes at HBM speed relative to MFMA time per key.
+      const double item_fixed = 96.0;
+      const double merge_per_row = 0.002 * in.D / 128.0;
+      double best = 1e300;
+      int32_t best_chunk = maxlen;
+      const int32_t max_cand = std::min<int32_t>(64, std::max<int32_t>(1, maxlen / kWideKeys));
+      for (int32_t cand = 1; cand <= max_cand; ++cand) {
+        const int32_t chunk = (int32_t)ceil_div(ceil_div(maxlen, cand), kWideKeys) * kWideKeys;
+        std::vector<double> cost;
+        double partial_rows = 0.0;
+        for (int32_t ui : wide_auto) {
+          const UnitDesc& u = P->units[ui];
+          const int32_t s = (int32_t)ceil_div(u.key_len, chunk);
+          std::vector<int32_t> bnd = shard_bounds(u.key_len, s, kWideKeys);
+          const int64_t M = (int64_t)u.n_tok * G;
+          for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
+            const int32_t kend = uw[ui].tile_key_end[t];
+            const int64_t rows = std::min<int64_t>(u.bm, M - (int64_t)t * u.bm);
+            int live = 0;
+            for (size_t k = 0; k + 1 < bnd.size(); ++k) {
+              if (bnd[k] >= kend) break;
+              ++live;
+              const int32_t keys = std::min(bnd[k + 1], kend) - bnd[k];
+              for (int32_t kv = 0; kv < in.H_kv; ++kv) cost.push_back(item_fixed + keys);
+            }
+            if (live > 1) partial_rows += (double)live * rows * in.H_kv;
+          }
+        }
+        const double total = lpt_makespan(cost, (int)slots) + merge_per_row * partial_rows;
+        if (total < best * 0.999) {
+          best = total;
+          best_chunk = chunk;
+        }
+      }
+      for (int32_t ui : wide_auto) S[ui] = (int32_t)ceil_div(P->units[ui].key_len, best_chunk);
+    }
+  }
+  for (int32_t ui = 0; ui < nu; ++ui)
+    if (override_of(ui) > 0) S[ui] = override_of(ui);
+
+  // Shard boundaries, live counts, workspace offsets, items.
+  P->api_splits.assign(ng + nb, 0);
+  P->unit_slot = api_slot;
+  int64_t part = 0;
+  for (int32_t ui = 0; ui < nu; ++ui) {
+    UnitDesc& u = P->units[ui];
+    const int32_t tile_keys = (u.bm == kWideRows) ? kWideKeys : kNarrowKeys;
+    std::vector<int32_t> bnd = shard_bounds(u.key_len, S[ui], tile_keys);
+    u.n_splits = (int32_t)bnd.size() - 1;
+    P->api_splits[api_slot[ui]] = u.n_splits;
+    P->max_splits = std::max(P->max_splits, u.n_splits);
+    u.tile_off = (int32_t)P->tiles.size();
+    const int64_t M = (int64_t)u.n_tok * G;
+    for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
+      const int32_t kend = uw[ui].tile_key_end[t];
+      int32_t live = 0;
+      while (live < u.n_splits && bnd[live] < kend) ++live;
+      TileInfo ti{};
+      ti.live = live;
+      ti.part_off = part;
+      part += (int64_t)in.H_kv * live * u.bm;
+      P->tiles.push_back(ti);
+      const int32_t row_begin = (int32_t)(t * u.bm);
+      const int32_t n_rows = (int32_t)std::min<int64_t>(u.bm, M - row_begin);
+      for (int32_t s = 0; s < live; ++s) {
+        for (int32_t kv = 0; kv < in.H_kv; ++kv) {
+          WorkItem w{};
+          w.unit = ui;
+          w.kv = kv;
+          w.row_begin = row_begin;
+          w.n_rows = n_rows;
+          w.key_begin = bnd[s];
+          w.key_end = std::min(bnd[s + 1], kend);
+          w.split = s;
+          w.tile = (int32_t)t;
+          P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
+          (u.bm == kWideRows ? P->wide : P->narrow).push_back(w);
+        }
+      }
+    }
+  }
+  P->part_rows = part;
+
+  // Largest items first, so the tail of the grid holds the short ones.
+  auto by_cost = [](const WorkItem& a, const WorkItem& b) {
+    const int32_t ka = a.key_end - a.key_begin, kb = b.key_end - b.key_begin;
+    if (ka != kb) return ka > kb;
+    if (a.unit != b.unit) return a.unit < b.unit;
+    if (a.split != b.split) return a.split < b.split;
+    if (a.kv != b.kv) return a.kv < b.kv;
+    return a.tile < b.tile;
+  };
+  std::stable_sort(P->wide.begin(), P->wide.end(), by_cost);
+  std::stable_sort(P->narrow.begin(), P->narrow.end(), by_cost);
+
+  // Output rows that need the merge kernel (two or more live partials).
+  for (int32_t b = 0; b < nb; ++b) {
+    const BranchDesc& br = P->branches[b];
+    for (int32_t t = 0; t < br.q_len; ++t) {
+      const int32_t tok = br.q_begin + t;
+      for (int32_t g = 0; g < G; ++g) {
+        int32_t n = 0;
+        for (int32_t ui : {br.unit_sh, br.unit_pr}) {
+          if (ui < 0) continue;
+          const UnitDesc& u = P->units[ui];
+          const int64_t r = (int64_t)(tok - u.tok_begin) * G + g;
+          n += P->tiles[u.tile_off + r / u.bm].live;
+        }
+        if (n >= 2) P->merge_rows += in.H_kv;
+      }
+    }
+  }
+  return "";
+}
+
+}  // namespace gqa

@@ -1,0 +1,177 @@
+/*
+ * gqa_attn.h -- C ABI of the MI355X (gfx950) shared-prefix GQA attention library.
+ *
+ * What one forward call computes
+ * ------------------------------
+ * Causal grouped-query attention with an online softmax over a shared-prefix
+ * KV cache, for agentic fan-out (AHBM Agentic Runtime Architecture, §1.1-§1.3
+ * and §3.1-§3.4; ADR-0060 GQA fused attention, TL;DR kernel and §3-§5):
+ *
+ *   - Branches are grouped; a group's branches share one prefix stored once.
+ *     Branch b's context is  shared[group(b)] ++ private(b),  where the
+ *     private suffix is read through the branch's page table (AHBM Agentic
+ *     Runtime Architecture, §3.1).
+ *   - Branch b brings q_len(b) new query tokens; they are the last q_len(b)
+ *     positions of its context, and key j of the context has position j.
+ *   - Query head h reads KV head floor(h / G), G = H_q / H_kv (ADR-0060, §0.5.3).
+ *   - z = softmax_scale * q.k; with causal != 0 key j is visible to the query
+ *     at position p iff j <= p (ADR-0060, §5.4), otherwise every key of the
+ *     branch's context is visible (§5.2).
+ *   - O = sum_j softmax(z)_j v_j in the storage dtype (round to nearest even),
+ *     LSE = ln(sum_j exp(z_j)) in fp32 (natural log, scaled-score units).
+ *
+ * Internally the library folds the G query heads of a KV head and the query
+ * tokens of all branches of a group into one M dimension (ADR-0060, §5.2;
+ * AHBM Agentic Runtime Architecture, §3.2), splits each KV range into shards
+ * whose (m, l, O) partials are combined by a log-sum-exp merge (ADR-0060,
+ * §4), and skips KV tiles that lie entirely in the future of a query block
+ * (ADR-0060, §5.4). None of that is visible in the result beyond rounding.
+ *
+ * Conventions
+ * -----------
+ * Pointers are DEVICE pointers unless the comment says (host). The caller owns
+ * every buffer; the library reads inputs, writes only `o` and `lse`, and never
+ * writes K/V (the cache is appended upstream before launch: ADR-0060, §0.5.1).
+ * Calls are stream-ordered and asynchronous: gqa_attn_forward returns without
+ * waiting for the GPU. Host arrays may be reused as soon as a call returns.
+ * One handle serves one stream at a time; concurrent calls on one handle race.
+ * Every entry point returns a gqa_status; on a negative status nothing was
+ * launched and gqa_attn_last_error() holds a message (thread-local).
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = -1,   /* a size, pointer, alignment or length is wrong */
+  GQA_ERR_UNSUPPORTED = -2,   /* valid request the library does not implement */
+  GQA_ERR_NO_MEMORY = -3,     /* workspace or plan buffers could not be allocated
+                                 (or would exceed workspace_bytes_cap)          */
+  GQA_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed     */
+} gqa_status;
+
+typedef enum {
+  GQA_BF16 = 0,               /* Q, K, V, O in bfloat16; bf16 MFMA, fp32 accumulate */
+  GQA_FP32 = 1                /* Q, K, V, O in float32; fp32 MFMA                   */
+} gqa_dtype;
+
+typedef struct {
+  int32_t num_q_heads;        /* H_q, > 0, a multiple of num_kv_heads              */
+  int32_t num_kv_heads;       /* H_kv, > 0                                         */
+  int32_t head_dim;           /* d: 64 or 128                                      */
+  int32_t page_size;          /* tokens per private page, 1..4096                  */
+  int32_t dtype;              /* gqa_dtype                                         */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(d) (ADR-0060, §0.5.3)         */
+  int64_t workspace_bytes_cap;/* cap on the split-partial workspace; 0 = no cap    */
+} gqa_attn_params;
+
+typedef struct gqa_attn gqa_attn;   /* opaque: plan buffers, workspace, timers */
+
+/* Create a handle for fixed head geometry and dtype. `p` (host) is copied.
+ * Errors: GQA_ERR_INVALID_ARG for bad parameters, GQA_ERR_UNSUPPORTED for a
+ * head_dim other than 64/128, GQA_ERR_HIP if no HIP device is usable. */
+gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out);
+
+/* One attention forward over a set of groups and branches.
+ *
+ *  q          [n_q_tokens, H_q, d]      branch b's q_len tokens are contiguous,
+ *                                       branches in order (n_q_tokens = sum q_len)
+ *  k_shared   [H_kv, n_shared_tokens, d]  shared prefixes of all groups,
+ *  v_shared                             concatenated along the token axis
+ *  k_pages    [n_pages, H_kv, page_size, d]  private-suffix page pool
+ *  v_pages
+ *  page_table [n_branches, max_pages_per_branch] int32 physical page ids;
+ *             entries past a branch's last page are ignored (pad with -1)
+ *  n_groups, group_shared_start (host), group_shared_len (host):
+ *             group g's prefix is tokens [start, start + len) of k_shared
+ *  n_branches, branch_group (host), branch_q_len (host),
+ *  branch_private_len (host): per branch; the branches of one group must be
+ *             consecutive, and 0 <= q_len <= shared_len + private_len
+ *  splits_override (host) [n_groups + n_branches] or NULL: KV shards per
+ *             unit -- one entry per group prefix, then one per branch suffix;
+ *             0 lets the library's split heuristic choose
+ *  causal     0 or 1
+ *  o          out [n_q_tokens, H_q, d] storage dtype
+ *  lse        out [n_q_tokens, H_q] float32, natural log
+ *  stream     hipStream_t (NULL = default stream)
+ *
+ * Sizes n_shared_tokens and n_pages are implied by the metadata; the page
+ * table's contents are a precondition (every id of a page a branch uses must
+ * be in [0, n_pages)); they are not checked on the device.
+ * Device pointers must be 16-byte aligned; a pointer whose extent is zero may
+ * be NULL. Errors: GQA_ERR_INVALID_ARG, GQA_ERR_NO_MEMORY (workspace growth),
+ * GQA_ERR_HIP (launch failure). The plan is rebuilt only when the metadata
+ * differs from the previous call on this handle. */
+gqa_status gqa_attn_forward(gqa_attn* h,
+                            const void* q,
+                            const void* k_shared, const void* v_shared,
+                            const void* k_pages, const void* v_pages,
+                            const int32_t* page_table, int32_t max_pages_per_branch,
+                            int32_t n_groups, const int32_t* group_shared_start,
+                            const int32_t* group_shared_len,
+                            int32_t n_branches, const int32_t* branch_group,
+                            const int32_t* branch_q_len, const int32_t* branch_private_len,
+                            const int32_t* splits_override,
+                            int32_t causal,
+                            void* o, float* lse,
+                            void* stream);
+
+/* Release the handle (waits for its outstanding work). NULL is accepted. */
+gqa_status gqa_attn_destroy(gqa_attn* h);
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char* gqa_attn_last_error(void);
+
+/* Summary of the plan used by the most recent forward on `h` (host). */
+typedef struct {
+  int64_t n_items_wide;       /* work items on the 128-row MFMA kernel            */
+  int64_t n_items_narrow;     /* work items on the 32-row decode kernel           */
+  int64_t n_kv_tiles;         /* (item, KV tile) pairs the kernels will process   */
+  int64_t n_merge_rows;       /* output rows (token, head) combined by the merge  */
+  int64_t workspace_bytes;    /* partial-state workspace in use                   */
+  int64_t n_units;            /* group prefixes + branch suffixes with keys       */
+  int32_t max_splits;         /* largest split count of any unit                  */
+  int32_t reserved;
+} gqa_plan_stats;
+gqa_status gqa_attn_plan_stats(const gqa_attn* h, gqa_plan_stats* out);
+
+/* Split count chosen for each unit by the last forward (host array of
+ * n_groups + n_branches entries, same order as splits_override; 0 for a
+ * unit without keys or without queries). */
+gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n);
+
+/* Kernel timing with HIP events recorded on the forward's stream around each
+ * kernel. enable != 0 starts recording (and clears earlier records).
+ * gqa_attn_kernel_times waits for the recorded events and returns the summed
+ * milliseconds of every forward since timing was enabled and the number of
+ * forwards, then clears the records. */
+gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable);
+gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
+                                 int64_t* n_forwards);
+
+/* Host-only planner check (no device use): plans the given metadata with
+ * the handle-free parameters `p` and writes, for every work item, the tuple
+ * (unit, kv_head, row_begin, n_rows, key_begin, key_end, split, kernel) into
+ * `items` (host, int32, 8 per item) when `items` is not NULL and `cap`
+ * allows. Returns the item count through *n_items and the per-unit split
+ * counts through `splits` (host, n_groups + n_branches entries, may be NULL). */
+gqa_status gqa_attn_plan_host(const gqa_attn_params* p,
+                              int32_t n_groups, const int32_t* group_shared_start,
+                              const int32_t* group_shared_len,
+                              int32_t n_branches, const int32_t* branch_group,
+                              const int32_t* branch_q_len, const int32_t* branch_private_len,
+                              const int32_t* splits_override, int32_t causal,
+                              int32_t* items, int64_t cap, int64_t* n_items,
+                              int32_t* splits, gqa_plan_stats* stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */
