@@ -1,0 +1,286 @@
+"""Benchmark of the shared-prefix GQA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fanout]
+
+A step is one forward of the whole path (plan reuse, attention kernels, LSE
+merge) over one batch of synthetic input already resident in HBM. The
+headline workload is the 8-agent fan-out (8 sub-agents x 20 new tokens over
+a 32768-token shared prefix, 512 private tokens each in 16-token pages,
+Llama3-70B heads: H_q 64, H_kv 8, d 128, bf16). Input copies are rotated so
+the K/V working set exceeds the 256 MB last-level cache and every step reads
+its K/V from HBM.
+
+Prints ONE JSON line: throughput (TFLOP/s on the algorithmic FLOP count),
+effective KV GB/s, the roofline of the dominant kernel (timed with HIP
+events recorded by the library on the forward's stream), the fp64 CPU oracle
+timed on a bounded sample on this host, and secondary lines for the other
+workloads (decode, prefill, mixed).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + KV GB/s (% of MI355X roofline), 8-agent fan-out GQA"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA (published)
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 matrix/vector (published)
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E (published)
+LLC_BYTES = 256 << 20           # Infinity Cache
+
+WORKLOADS = {"fanout": 3, "decode": 2, "prefill": 4, "mixed": 5, "tiny": 1}
+KERNEL_SOURCES = ["gqa_attention_agentic_amd/csrc/attention.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def clone_inputs(inp, n):
+    from workload.generate import Inputs
+    out = [inp]
+    for _ in range(n - 1):
+        out.append(Inputs(inp.q.clone(), inp.k_shared.clone(), inp.v_shared.clone(), inp.k_pages.clone(),
+                          inp.v_pages.clone(), inp.page_table.clone(), inp.group_shared_start,
+                          inp.group_shared_len, inp.branch_group, inp.branch_q_len,
+                          inp.branch_private_len))
+    return out
+
+
+def run_workload(k: int, steps: int, warmup: int, log):
+    """Times `steps` forwards of config k; returns a result dict."""
+    import torch
+
+    import gqa_attention_agentic_amd as G
+    from workload import generate, get_config
+
+    w = get_config(k)
+    t0 = time.time()
+    base = generate(w, "cuda")
+    kv_bytes = w.kv_bytes()
+    n_copies = max(1, min(8, -(-2 * LLC_BYTES // max(1, kv_bytes))))
+    if kv_bytes > 4 * LLC_BYTES:
+        n_copies = 1
+    copies = clone_inputs(base, n_copies)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs ready ({n_copies} copies, {time.time() - t0:.1f}s)")
+    h = G.GqaAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype)
+    out = torch.empty_like(base.q)
+    lse = torch.empty(base.q.shape[0], w.num_q_heads, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        h.forward_inputs(copies[i % n_copies], w.causal, splits=w.splits, out=out, lse=lse,
+                         stream=stream.cuda_stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    h.enable_timing(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = start.elapsed_time(end) / steps
+    attn_ms, merge_ms, n = h.kernel_times()
+    h.enable_timing(False)
+    attn_ms /= max(1, n)
+    merge_ms /= max(1, n)
+    stats = h.plan_stats()
+    flops = w.flops()
+    res = {
+        "workload": w.name,
+        "description": w.description,
+        "flops": flops,
+        "kv_bytes": kv_bytes,
+        "io_bytes": w.io_bytes(),
+        "ms_per_step": wall_ms,
+        "attn_kernel_ms": attn_ms,
+        "merge_kernel_ms": merge_ms,
+        "tflops": flops / (wall_ms * 1e-3) / 1e12,
+        "kv_gbps": kv_bytes / (wall_ms * 1e-3) / 1e9,
+        "attn_kernel_tflops": flops / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None,
+        "plan": stats,
+        "splits": h.plan_splits()[:8],
+        "input_copies": n_copies,
+        "dtype": w.dtype,
+    }
+    log(f"[bench] {w.name}: {wall_ms:.4f} ms/step, attention {attn_ms:.4f} ms, merge {merge_ms:.4f} ms, "
+        f"{res['tflops']:.1f} TFLOP/s, KV {res['kv_gbps']:.0f} GB/s")
+    h.close()
+    del copies, base
+    torch.cuda.empty_cache()
+    return w, res
+
+
+def roofline_of(w, res, traffic):
+    """Roofline of the dominant kernel (attention) from its HIP-event time."""
+    t = res["attn_kernel_ms"] * 1e-3
+    peak_mfma = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    intensity = w.flops() / (w.kv_bytes() + w.io_bytes())
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if intensity >= ridge:
+        achieved = w.flops() / t / 1e12
+        return {"bound": "mfma", "achieved": achieved, "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": achieved / peak_mfma, "traffic": traffic}
+    achieved = (w.kv_bytes() + w.io_bytes()) / t / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic}
+
+
+def traffic_for(w):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(k: int, budget_s: float, log):
+    """The fp64 oracle on this host's cores over whole branches of the same
+    workload until about budget_s seconds of CPU work (input generation and
+    copies excluded)."""
+    import torch
+
+    import oracle
+    from workload import generate, get_config
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import cpu_subset
+
+    w = get_config(k)
+    torch.set_num_threads(os.cpu_count() or 1)
+    inp = generate(w, "cpu")
+    done_flops, spent, branches = 0, 0.0, []
+    qb = [0]
+    for b in w.branches:
+        qb.append(qb[-1] + b.q_len)
+    order = sorted(range(len(w.branches)), key=lambda b: -w.branches[b].q_len)
+    for b in order:
+        if spent >= budget_s:
+            break
+        br = w.branches[b]
+        if br.q_len == 0:
+            continue
+        sub, _ = cpu_subset(inp, [b])
+        t0 = time.perf_counter()
+        if k == 4:   # prefill: a bounded row sample across the whole sequence
+            toks = list(range(0, br.q_len, max(1, br.q_len // 48)))
+            oracle.attention(sub, w.num_kv_heads, w.page_size, w.causal, tokens=toks)
+            C = w.context_len(br)
+            pairs = sum((C - br.q_len + t + 1) if w.causal else C for t in toks)
+        else:
+            oracle.attention(sub, w.num_kv_heads, w.page_size, w.causal)
+            C = w.context_len(br)
+            pairs = sum((C - br.q_len + t + 1) if w.causal else C for t in range(br.q_len))
+        spent += time.perf_counter() - t0
+        done_flops += 4 * w.head_dim * w.num_q_heads * pairs
+        branches.append(b)
+    value = done_flops / spent / 1e12
+    sample = (f"{len(branches)} of {len(w.branches)} branches of {w.name} "
+              f"({done_flops / 1e9:.1f} GFLOP, all {w.num_q_heads} heads, fp64, {spent:.1f}s)")
+    log(f"[bench] cpu oracle: {value * 1e3:.2f} GFLOP/s on {sample}")
+    return {"value": value, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": sample, "cpu": cpu_model(), "os_cpu_count": os.cpu_count(), "seconds": spent}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fanout", choices=sorted(WORKLOADS))
+    ap.add_argument("--others", default="decode,prefill,mixed",
+                    help="comma list of secondary workloads ('' for none)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gqa_attention_agentic_amd as G
+    G.load()
+
+    k = WORKLOADS[args.workload]
+    w, res = run_workload(k, args.steps, args.warmup, log)
+    traffic = traffic_for(w)
+    others = {}
+    for name in [x for x in args.others.split(",") if x and x != args.workload]:
+        ko = WORKLOADS[name]
+        wo, ro = run_workload(ko, max(3, args.steps // 4), 2, log)
+        ro["roofline"] = roofline_of(wo, ro, traffic_for(wo))
+        others[name] = ro
+    line = {
+        "metric": METRIC,
+        "value": res["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic N(0,1), seeded; shapes of the Llama3-70B attention layer",
+        "config": {"workload": w.name, "agents": len(w.branches), "new_tokens_per_agent": w.branches[0].q_len,
+                   "shared_prefix": w.groups[0].shared_len, "private_suffix": w.branches[0].private_len,
+                   "page_size": w.page_size, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "causal": w.causal, "parallelism": "single GPU"},
+        "kv_gbps": res["kv_gbps"],
+        "kv_frac_of_hbm_peak": res["kv_gbps"] / PEAK_HBM_GBPS,
+        "attn_kernel_ms": res["attn_kernel_ms"],
+        "merge_kernel_ms": res["merge_kernel_ms"],
+        "roofline": roofline_of(w, res, traffic),
+        "kernel_source_hash": kernel_hash(),
+        "plan": res["plan"],
+        "splits": res["splits"],
+        "input_copies": res["input_copies"],
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(k, args.cpu_budget, log)
+    line["others"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -83,7 +83,7 @@ class GqaAttention:
         _check_lengths(ng, nb, group_shared_len, branch_q_len, branch_private_len, splits)
         ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() > 0 else 0)
         st = self.lib.gqa_attn_forward(
-            self._h, ptr(q), ptr(k_shared), ptr(v_shared), ptr(k_pages), ptr(v_pages), ptr(page_table),
+            self._h, ptr(q), ptr(k_shared), ptr(v_shared), int(k_shared.shape[1]), ptr(k_pages), ptr(v_pages), ptr(page_table),
             int(page_table.shape[1]) if page_table.dim() == 2 else 0,
             ng, _lib.int_array(group_shared_start), _lib.int_array(group_shared_len),
             nb, _lib.int_array(branch_group), _lib.int_array(branch_q_len),

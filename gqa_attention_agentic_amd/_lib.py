@@ -69,7 +69,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     P, I32, I64, VP = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.gqa_attn_create.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(P)]
-    lib.gqa_attn_forward.argtypes = [P, VP, VP, VP, VP, VP, VP, I32, I32, I32P, I32P, I32, I32P, I32P,
+    lib.gqa_attn_forward.argtypes = [P, VP, VP, VP, I32, VP, VP, VP, I32, I32, I32P, I32P, I32, I32P, I32P,
                                      I32P, I32P, I32, VP, VP, VP]
     lib.gqa_attn_destroy.argtypes = [P]
     lib.gqa_attn_last_error.restype = ctypes.c_char_p

@@ -254,7 +254,7 @@ gqa_status gqa_attn_destroy(gqa_attn* h) {
 }
 
 gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, const void* v_shared,
-                            const void* k_pages, const void* v_pages, const int32_t* page_table,
+                            int32_t n_shared_tokens, const void* k_pages, const void* v_pages, const int32_t* page_table,
                             int32_t max_pages_per_branch, int32_t n_groups,
                             const int32_t* group_shared_start, const int32_t* group_shared_len,
                             int32_t n_branches, const int32_t* branch_group, const int32_t* branch_q_len,
@@ -295,13 +295,18 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   if (any_q && (!q || !o || !lse)) return fail(GQA_ERR_INVALID_ARG, "q, o and lse must be non-NULL");
   if (P.n_shared_tokens > 0 && (!k_shared || !v_shared))
     return fail(GQA_ERR_INVALID_ARG, "k_shared and v_shared must be non-NULL");
+  if (n_shared_tokens < P.n_shared_tokens)
+    return fail(GQA_ERR_INVALID_ARG, "a group's shared range ends past n_shared_tokens");
   if (any_priv && (!k_pages || !v_pages || !page_table))
     return fail(GQA_ERR_INVALID_ARG, "k_pages, v_pages and page_table must be non-NULL");
   if (any_priv && max_pages_per_branch < P.max_branch_pages)
     return fail(GQA_ERR_INVALID_ARG, "max_pages_per_branch is smaller than a branch's page count");
-  const void* ptrs[] = {q, k_shared, v_shared, k_pages, v_pages, page_table, o, lse};
+  const void* ptrs[] = {q, k_shared, v_shared, k_pages, v_pages, o};
   for (const void* ptr : ptrs)
-    if (ptr && !aligned16(ptr)) return fail(GQA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    if (ptr && !aligned16(ptr)) return fail(GQA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if ((page_table && (reinterpret_cast<uintptr_t>(page_table) & 3u)) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(GQA_ERR_INVALID_ARG, "page_table and lse must be 4-byte aligned");
   if (!any_q) return GQA_OK;
 
   hipError_t e = hipSetDevice(h->device);
@@ -340,7 +345,7 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   a.H_q = h->p.num_q_heads;
   a.H_kv = h->p.num_kv_heads;
   a.G = a.H_q / a.H_kv;
-  a.n_shared = Q.n_shared_tokens;
+  a.n_shared = n_shared_tokens;
   a.page_size = h->p.page_size;
   a.page_shift = -1;
   for (int sft = 0; sft < 13; ++sft)

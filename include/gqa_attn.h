@@ -84,6 +84,8 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out);
  *                                       branches in order (n_q_tokens = sum q_len)
  *  k_shared   [H_kv, n_shared_tokens, d]  shared prefixes of all groups,
  *  v_shared                             concatenated along the token axis
+ *  n_shared_tokens  token extent (stride) of k_shared / v_shared; every
+ *             group's [start, start + len) must lie inside it
  *  k_pages    [n_pages, H_kv, page_size, d]  private-suffix page pool
  *  v_pages
  *  page_table [n_branches, max_pages_per_branch] int32 physical page ids;
@@ -101,16 +103,16 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out);
  *  lse        out [n_q_tokens, H_q] float32, natural log
  *  stream     hipStream_t (NULL = default stream)
  *
- * Sizes n_shared_tokens and n_pages are implied by the metadata; the page
- * table's contents are a precondition (every id of a page a branch uses must
- * be in [0, n_pages)); they are not checked on the device.
- * Device pointers must be 16-byte aligned; a pointer whose extent is zero may
- * be NULL. Errors: GQA_ERR_INVALID_ARG, GQA_ERR_NO_MEMORY (workspace growth),
+ * The page table's contents are a precondition (every id of a page a branch
+ * uses must be a page of the pool); they are not checked on the device.
+ * q, k/v and o must be 16-byte aligned, page_table and lse 4-byte aligned;
+ * a pointer whose extent is zero may be NULL. Errors: GQA_ERR_INVALID_ARG, GQA_ERR_NO_MEMORY (workspace growth),
  * GQA_ERR_HIP (launch failure). The plan is rebuilt only when the metadata
  * differs from the previous call on this handle. */
 gqa_status gqa_attn_forward(gqa_attn* h,
                             const void* q,
                             const void* k_shared, const void* v_shared,
+                            int32_t n_shared_tokens,
                             const void* k_pages, const void* v_pages,
                             const int32_t* page_table, int32_t max_pages_per_branch,
                             int32_t n_groups, const int32_t* group_shared_start,

@@ -184,6 +184,7 @@ def test_config3_sampled():
     _sample_parity(3, list(range(8)), toks)
 
 
+@pytest.mark.timeout(600)
 def test_config4_sampled():
     rng = random.Random(4)
     # shard boundaries (4096 multiples), KV tile edges, M-tile edges, the last rows
@@ -192,6 +193,7 @@ def test_config4_sampled():
     _sample_parity(4, [0], sorted(toks))
 
 
+@pytest.mark.timeout(600)
 def test_config5_sampled():
     w = get_config(5)
     rng = random.Random(5)
