@@ -22,6 +22,10 @@ ARCH = "gfx950"
 
 SOURCES = ["attention.hip", "api.cpp", "plan.cpp"]
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Kernels run with the IEEE mode bit off: max/min then need no NaN-quieting
+# canonicalisation of their inputs. The kernels never produce NaN themselves
+# (masked scores are -inf and the -inf - -inf case is guarded).
+KERNEL_FP = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
 
 
 def hipcc() -> str:
@@ -42,6 +46,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         path = os.path.join(CSRC, src)
         obj = os.path.join(bdir, src + ".o")
         cmd = [cc] + common + NO_PACKED_FP32
+        if src.endswith(".hip"):
+            cmd += KERNEL_FP
         if src.endswith(".hip") and resource_usage:
             cmd += ["-Rpass-analysis=kernel-resource-usage"]
         cmd += ["-c", path, "-o", obj]

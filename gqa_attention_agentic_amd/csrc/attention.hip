@@ -103,6 +103,9 @@ struct Cfg {
   static constexpr int QF = BF16 ? D / 16 : D / 2;              // Q fragments per lane
   static constexpr int MERGE = NARROW ? 4 * (OB * 16 * 64 + 2 * 64) * 4 : 0;
   static constexpr int LDS = (STAGE * NSTAGE > MERGE) ? STAGE * NSTAGE : MERGE;
+  // Two workgroups per CU (8 waves, 2 per SIMD) when their LDS fits; the
+  // register budget then is 256 per lane.
+  static constexpr int WAVES_PER_SIMD = (!NARROW && 2 * LDS <= 160 * 1024) ? 2 : 1;
   static_assert(CHUNKS % LOADERS == 0, "tile does not split evenly over the loaders");
   static_assert(!BF16 || CPT == 2 || CPT % 4 == 0, "V transpose needs 2 or a multiple of 4 keys per thread");
   static_assert(LDS <= 160 * 1024, "LDS budget of a gfx950 CU exceeded");
@@ -122,54 +125,109 @@ struct State {
   float l;   // running sum
 };
 
-template <int D>
-__device__ __forceinline__ int64_t kv_offset(const AttnArgs& a, const UnitDesc& u, int kv, int key) {
-  if (u.kind == kShared) return ((int64_t)kv * a.n_shared + u.src + key) * D;
-  int lp, slot;
-  if (a.page_shift >= 0) {
-    lp = key >> a.page_shift;
-    slot = key & (a.page_size - 1);
+// Per-item K/V source: the shared prefix rows of one KV head (contiguous
+// keys), or the branch's pages (one page-table lookup per key).
+template <typename T>
+struct KvSrc {
+  const T* kb;            // shared: k_shared + (kv * n_shared + src) * D;  paged: k_pages + kv * ps * D
+  const T* vb;
+  const int32_t* table;   // paged: the branch's page-table row
+  int64_t page_elems;     // paged: elements per page (H_kv * ps * D)
+  int ps, shift;          // paged: page size and log2(page size) (-1 if not a power of two)
+  bool paged;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ KvSrc<T> kv_src(const AttnArgs& a, const UnitDesc& u, int kv) {
+  KvSrc<T> s;
+  s.paged = u.kind != kShared;
+  s.ps = a.page_size;
+  s.shift = a.page_shift;
+  if (!s.paged) {
+    const int64_t base = ((int64_t)kv * a.n_shared + u.src) * D;
+    s.kb = (const T*)a.k_shared + base;
+    s.vb = (const T*)a.v_shared + base;
+    s.table = nullptr;
+    s.page_elems = 0;
   } else {
-    lp = key / a.page_size;
-    slot = key - lp * a.page_size;
+    const int64_t base = (int64_t)kv * a.page_size * D;
+    s.kb = (const T*)a.k_pages + base;
+    s.vb = (const T*)a.v_pages + base;
+    s.table = a.page_table + (int64_t)u.src * a.max_pages;
+    s.page_elems = (int64_t)a.H_kv * a.page_size * D;
   }
-  const int page = a.page_table[(int64_t)u.src * a.max_pages + lp];
-  return (((int64_t)page * a.H_kv + kv) * a.page_size + slot) * D;
+  return s;
+}
+
+// Element offset of unit-local key `key` in the source.
+template <typename T, int D, bool PAGED>
+__device__ __forceinline__ int64_t key_off(const KvSrc<T>& s, int key) {
+  if (!PAGED) return (int64_t)key * D;
+  int lp, slot;
+  if (s.shift >= 0) {
+    lp = key >> s.shift;
+    slot = key & (s.ps - 1);
+  } else {
+    lp = key / s.ps;
+    slot = key - lp * s.ps;
+  }
+  return (int64_t)s.table[lp] * s.page_elems + (int64_t)slot * D;
 }
 
 // Global -> registers for the KV tile whose first unit-local key is key0.
-// Keys at or past key_end are not read (the ragged tail is zero-filled).
-template <class C, typename T, int D>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const UnitDesc& u, int kv, int key0,
-                                          int key_end, int ltid, Stage<C>& st) {
-  const T* kb = (const T*)(u.kind == kShared ? a.k_shared : a.k_pages);
-  const T* vb = (const T*)(u.kind == kShared ? a.v_shared : a.v_pages);
+// Each thread loads CPT 16-byte chunks of K (consecutive lanes read
+// consecutive chunks of a key row) and, for bf16, CPT consecutive keys of
+// one 8-wide d slice of V (so it can write them transposed). Keys at or past
+// key_end are not read (zero-filled) -- only checked when RAGGED.
+template <class C, typename T, int D, bool PAGED, bool RAGGED>
+__device__ __forceinline__ void load_tile_t(const KvSrc<T>& s, int key0, int key_end, int ltid,
+                                            Stage<C>& st) {
   constexpr int CPR = D / C::VEC;   // chunks per key row
 #pragma unroll
   for (int j = 0; j < C::CPT; ++j) {
     const int c = ltid + C::LOADERS * j;
     const int key = key0 + c / CPR;
     const int col = (c % CPR) * C::VEC;
-    if (key < key_end) {
-      const int64_t off = kv_offset<D>(a, u, kv, key) + col;
-      st.k[j] = *(const uint4*)(kb + off);
-      if (!C::BF16) st.v[j] = *(const uint4*)(vb + off);
+    if (!RAGGED || key < key_end) {
+      const int64_t off = key_off<T, D, PAGED>(s, key) + col;
+      st.k[j] = *(const uint4*)(s.kb + off);
+      if (!C::BF16) st.v[j] = *(const uint4*)(s.vb + off);
     } else {
       st.k[j] = make_uint4(0, 0, 0, 0);
       if (!C::BF16) st.v[j] = make_uint4(0, 0, 0, 0);
     }
   }
   if (C::BF16) {
-    // V: each thread takes CPT consecutive keys of one 8-wide d slice, so
-    // that it can write them transposed.
     constexpr int KG = C::BN / C::CPT;
     const int kg = ltid % KG, oct = ltid / KG;
+    const int k0 = key0 + kg * C::CPT;
+    // CPT consecutive keys starting at a multiple of CPT never straddle a
+    // page when the page size is a power-of-two multiple of CPT; otherwise
+    // each key is looked up.
+    const bool one_page = !PAGED || (s.shift >= 0 && s.ps >= C::CPT && (key0 & (C::CPT - 1)) == 0);
+    const int64_t base = one_page ? key_off<T, D, PAGED>(s, k0) : 0;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int key = key0 + kg * C::CPT + i;
-      if (key < key_end) st.v[i] = *(const uint4*)(vb + kv_offset<D>(a, u, kv, key) + oct * 8);
-      else st.v[i] = make_uint4(0, 0, 0, 0);
+      const int key = k0 + i;
+      if (!RAGGED || key < key_end) {
+        const int64_t off = (one_page ? base + (int64_t)i * D : key_off<T, D, PAGED>(s, key)) + oct * 8;
+        st.v[i] = *(const uint4*)(s.vb + off);
+      } else {
+        st.v[i] = make_uint4(0, 0, 0, 0);
+      }
     }
+  }
+}
+
+template <class C, typename T, int D>
+__device__ __forceinline__ void load_tile(const KvSrc<T>& s, int key0, int key_end, int ltid, Stage<C>& st) {
+  const bool ragged = key0 + C::BN > key_end;
+  if (s.paged) {
+    if (ragged) load_tile_t<C, T, D, true, true>(s, key0, key_end, ltid, st);
+    else load_tile_t<C, T, D, true, false>(s, key0, key_end, ltid, st);
+  } else {
+    if (ragged) load_tile_t<C, T, D, false, true>(s, key0, key_end, ltid, st);
+    else load_tile_t<C, T, D, false, false>(s, key0, key_end, ltid, st);
   }
 }
 
@@ -228,16 +286,20 @@ __device__ __forceinline__ void store_tile(T* Ks, T* Vs, int ltid, const Stage<C
 }
 
 // One KV tile for one wave's 32 rows: S^T, mask, online softmax, O^T += V^T P^T.
-template <class C, typename T, int D>
-__device__ __forceinline__ void compute_tile(const T* Ks, const T* Vs, State<C>& s, int tile_key0,
-                                             int n_valid, bool need_mask, int causal, int key_pos0,
-                                             int row_pos, float scale_log2, int i, int h) {
+// Scores stay unscaled until the exponent: p = exp2(s * c - m) with
+// c = softmax_scale * log2(e) and the running max m kept in those units.
+template <class C, typename T, int D, bool MASK>
+__device__ __forceinline__ void compute_tile(const T* Ks, const T* Vs, State<C>& s, int kpos0,
+                                             int n_valid, int causal, int row_pos, float c, int i,
+                                             int h) {
   f32x16_t sacc[C::SB];
 #pragma unroll
   for (int kb = 0; kb < C::SB; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
     if constexpr (C::BF16) {
+      // Bound how many K operands the scheduler keeps in flight (register budget).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8_t av = *(const bf16x8_t*)(Ks + (32 * kb + i) * C::KP + 16 * ks + 8 * h);
@@ -251,54 +313,63 @@ __device__ __forceinline__ void compute_tile(const T* Ks, const T* Vs, State<C>&
       }
     }
   }
-  // scale into log2 units, mask, row max
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool vis = kl < n_valid && (!causal || kpos0 + kl <= row_pos);
+        sacc[kb][r] = vis ? sacc[kb][r] : kNegInf;
+      }
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
-  for (int kb = 0; kb < C::SB; ++kb) {
+  for (int kb = 0; kb < C::SB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = sacc[kb][r] * scale_log2;
-      if (need_mask) {
-        const int kl = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool vis = kl < n_valid && (!causal || key_pos0 + tile_key0 + kl <= row_pos);
-        v = vis ? v : kNegInf;
-      }
-      sacc[kb][r] = v;
-      mx = fmaxf(mx, v);
-    }
-  }
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(s.m, mx);
+  const float m_new = fmaxf(s.m, mx * c);
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
   const float corr = exp2_fast(s.m - m_use);
-  float rs = 0.f;
+  float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < C::SB; ++kb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(sacc[kb][r] - m_use);
-      sacc[kb][r] = p;
-      rs += p;
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -m_use));
+      const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
+      sacc[kb][r] = p0;
+      sacc[kb][r + 1] = p1;
+      rs0 += p0;
+      rs1 += p1;
     }
   }
+  float rs = rs0 + rs1;
   rs += __shfl_xor(rs, 32);
   s.l = s.l * corr + rs;
   s.m = m_new;
+  // The running max rarely moves after the first tiles: skip the O rescale
+  // when it moved for no row of the wave.
+  if (__builtin_amdgcn_ballot_w64(corr != 1.f) != 0) {
 #pragma unroll
-  for (int db = 0; db < C::OB; ++db) s.o[db] *= corr;
+    for (int db = 0; db < C::OB; ++db) s.o[db] *= corr;
+  }
 
   if constexpr (C::BF16) {
 #pragma unroll
     for (int kb = 0; kb < C::SB; ++kb) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int cc = 0; cc < 2; ++cc) {
         bf16x8_t pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * c + e];
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * cc + e];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < C::OB; ++db) {
           const bf16x8_t av =
-              *(const bf16x8_t*)(Vs + (32 * db + i) * C::VP + (2 * kb + c) * 16 + 8 * h);
+              *(const bf16x8_t*)(Vs + (32 * db + i) * C::VP + (2 * kb + cc) * 16 + 8 * h);
           s.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, s.o[db], 0, 0, 0);
         }
       }
@@ -317,6 +388,20 @@ __device__ __forceinline__ void compute_tile(const T* Ks, const T* Vs, State<C>&
       }
     }
   }
+}
+
+// Tile dispatch: the mask is only built for tiles that cross the causal
+// diagonal or the ragged end of the shard (ADR-0060, §5.4: all-past tiles
+// carry no mask; all-future tiles were skipped by the caller).
+template <class C, typename T, int D>
+__device__ __forceinline__ void run_tile(const T* Ks, const T* Vs, State<C>& s, const UnitDesc& u,
+                                         int tk0, int key_end, int causal, int row_pos, int pmin,
+                                         float c, int i, int h) {
+  const int nvalid = min(C::BN, key_end - tk0);
+  const int kpos0 = u.key_pos0 + tk0;
+  const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
+  if (need_mask) compute_tile<C, T, D, true>(Ks, Vs, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  else compute_tile<C, T, D, false>(Ks, Vs, s, kpos0, nvalid, causal, row_pos, c, i, h);
 }
 
 // Per-lane row bookkeeping.
@@ -416,13 +501,13 @@ __device__ __forceinline__ void wave_pos_range(const Row& w, int* pmin, int* pma
     lo = min(lo, __shfl_xor(lo, x));
     hi = max(hi, __shfl_xor(hi, x));
   }
-  *pmin = lo;
-  *pmax = hi;
+  *pmin = __builtin_amdgcn_readfirstlane(lo);   // wave-uniform: keep in SGPRs
+  *pmax = __builtin_amdgcn_readfirstlane(hi);
 }
 
 // ---------------------------------------------------------------- wide ----
 template <typename T, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, (Cfg<T, D, false>::WAVES_PER_SIMD))
 attn_wide(AttnArgs a) {
   using C = Cfg<T, D, false>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -436,24 +521,22 @@ attn_wide(AttnArgs a) {
   int pmin, pmax;
   wave_pos_range(w, &pmin, &pmax);
   const bool wave_rows = wave * 32 < it.n_rows;
+  const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
 
-  const int nkeys = it.key_end - it.key_begin;
-  const int nt = (nkeys + C::BN - 1) / C::BN;
+  const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;
   Stage<C> st;
-  load_tile<C, T, D>(a, u, it.kv, it.key_begin, it.key_end, tid, st);
+  load_tile<C, T, D>(src, it.key_begin, it.key_end, tid, st);
   store_tile<C, T, D>((T*)smem, (T*)(smem + C::K_ELEMS * sizeof(T)), tid, st);
   __syncthreads();
   for (int j = 0; j < nt; ++j) {
     const bool more = j + 1 < nt;
-    if (more) load_tile<C, T, D>(a, u, it.kv, it.key_begin + (j + 1) * C::BN, it.key_end, tid, st);
-    const int tk0 = it.key_begin + j * C::BN;                  // unit-local first key of the tile
-    const int nvalid = min(C::BN, it.key_end - tk0);
+    if (more) load_tile<C, T, D>(src, it.key_begin + (j + 1) * C::BN, it.key_end, tid, st);
+    const int tk0 = it.key_begin + j * C::BN;       // unit-local first key of the tile
     const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
     if (wave_rows && !future) {
-      const bool need_mask = (nvalid < C::BN) || (a.causal && u.key_pos0 + tk0 + C::BN - 1 > pmin);
       char* stg = smem + (j & 1) * C::STAGE;
-      compute_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, tk0, nvalid,
-                            need_mask, a.causal, u.key_pos0, w.pos, a.scale_log2, i, h);
+      run_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, u, tk0, it.key_end,
+                        a.causal, w.pos, pmin, a.scale_log2, i, h);
     }
     if (more) {
       char* stg = smem + ((j + 1) & 1) * C::STAGE;
@@ -464,9 +547,275 @@ attn_wide(AttnArgs a) {
   write_row<C, T, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
 }
 
+// ------------------------------------------------------ wide, bf16, DMA ----
+// The MFMA-bound kernel for bf16: 8 waves (256 rows, 32 per wave, 2 waves
+// per SIMD) share a 3-stage ring of 64-key K/V tiles in LDS that global->LDS
+// DMA (global_load_lds_dwordx4) fills two tiles ahead of the compute, with
+// no register staging. LDS rows are unpadded and XOR-swizzled per 16-byte
+// chunk so that both operand reads are bank-conflict free: K by the key's
+// low 3 bits (ds_read_b128 of 8 consecutive keys hits 8 distinct chunks), V
+// by 2x the key's low 2 bits (the 16-lane groups of ds_read_b64_tr_b16 read
+// 4 keys x 32 bytes, landing in 4 distinct 32-byte bank segments). The
+// transposing LDS read turns V's [key][d] rows into the k-contiguous operand
+// of O^T += V^T P^T without any transpose on the store side.
+template <int D>
+struct DmaCfg {
+  static constexpr bool BF16 = true;
+  static constexpr int WAVES = 8;
+  static constexpr int BM = 32 * WAVES;             // rows per item
+  static constexpr int BN = 64;                     // keys per tile
+  static constexpr int ROW = D * 2;                 // bytes per key row
+  static constexpr int TB = BN * ROW;               // bytes per tensor per tile
+  static constexpr int NINST = TB / 1024;           // 1 KB wave-instructions per tensor per tile
+  static constexpr int PER_WAVE = NINST / WAVES;    // per tensor per wave
+  static constexpr int VM_PER_TILE = 2 * PER_WAVE;  // DMA instructions per thread per tile
+  static constexpr int OB = D / 32, QF = D / 16, SB = BN / 32;
+  static_assert(NINST % WAVES == 0, "tile must split evenly over the waves");
+  static_assert(BM == kWideRowsBf16, "planner and kernel disagree on the M-tile");
+};
+
+// s_waitcnt immediate: vmcnt(vm), expcnt(7), lgkmcnt(0).
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define GQA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int D>
+struct DmaLane {
+  // per-lane constants of the DMA (global side) and of the operand reads (LDS side)
+  int key_rel[DmaCfg<D>::PER_WAVE];   // tile-relative key of this lane's chunk in instruction q
+  int colK[DmaCfg<D>::PER_WAVE];      // element offset inside the key row (logical chunk * 8)
+  int colV[DmaCfg<D>::PER_WAVE];
+  int kaddr[4];                       // byte offset of K operand chunk for ks = 0..3 (ks+4: +128)
+  int vaddr[2];                       // byte offset of the V tr16 read for db = 0, 1 (db+2: +128)
+};
+
+template <int D>
+__device__ __forceinline__ DmaLane<D> dma_lane(int wave, int lane) {
+  using C = DmaCfg<D>;
+  DmaLane<D> L;
+#pragma unroll
+  for (int q = 0; q < C::PER_WAVE; ++q) {
+    const int byte = (wave * C::PER_WAVE + q) * 1024 + 16 * lane;
+    const int kr = byte / C::ROW;
+    const int pc = (byte % C::ROW) / 16;
+    L.key_rel[q] = kr;
+    L.colK[q] = (pc ^ (kr & 7)) * 8;
+    L.colV[q] = (pc ^ (2 * (kr & 3))) * 8;
+  }
+  const int i = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) L.kaddr[ks] = i * C::ROW + 16 * ((2 * ks + h) ^ (i & 7));
+  const int g = lane >> 4, j = lane & 15, half = g & 1, hh = g >> 1;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+    L.vaddr[db] = (4 * hh + (j >> 2)) * C::ROW + 16 * ((4 * db + 2 * half + ((j >> 1) & 1)) ^ (2 * (j >> 2))) +
+                  8 * (j & 1);
+  return L;
+}
+
+// Issue the DMA of tile `t` (unit-local first key key0) into one ring stage.
+// Keys past key_end are clamped to the last valid key (finite data, masked
+// later). Paged sources with power-of-two pages of >= 16 tokens read the
+// tile's page ids with scalar loads, so no vector-memory wait is needed
+// before the addresses are formed.
+template <int D, bool PAGED, bool SCALAR_PAGES>
+__device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLane<D>& L, int wave, int key0,
+                                         int key_end, char* Kst, char* Vst) {
+  using C = DmaCfg<D>;
+  int pg[5] = {0, 0, 0, 0, 0};
+  int lp0 = 0;
+  if (PAGED && SCALAR_PAGES) {
+    lp0 = key0 >> src.shift;
+    const int lp_last = (key_end - 1) >> src.shift;
+#pragma unroll
+    for (int e = 0; e < 5; ++e) pg[e] = src.table[min(lp0 + e, lp_last)];
+  }
+#pragma unroll
+  for (int q = 0; q < C::PER_WAVE; ++q) {
+    const int k = min(key0 + L.key_rel[q], key_end - 1);
+    int64_t off;
+    if (!PAGED) {
+      off = (int64_t)k * D;
+    } else if (SCALAR_PAGES) {
+      const int e = (k >> src.shift) - lp0;
+      int page = pg[0];
+      page = (e == 1) ? pg[1] : page;
+      page = (e == 2) ? pg[2] : page;
+      page = (e == 3) ? pg[3] : page;
+      page = (e == 4) ? pg[4] : page;
+      off = (int64_t)page * src.page_elems + (int64_t)(k & (src.ps - 1)) * D;
+    } else {
+      off = key_off<uint16_t, D, true>(src, k);
+    }
+    const int n = wave * C::PER_WAVE + q;
+    __builtin_amdgcn_global_load_lds((const void*)(src.kb + off + L.colK[q]), GQA_LDS(Kst + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src.vb + off + L.colV[q]), GQA_LDS(Vst + n * 1024), 16, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const DmaLane<D>& L, int wave, int key0,
+                                             int key_end, char* Kst, char* Vst) {
+  if (!src.paged) dma_tile<D, false, false>(src, L, wave, key0, key_end, Kst, Vst);
+  else if (src.shift >= 4) dma_tile<D, true, true>(src, L, wave, key0, key_end, Kst, Vst);
+  else dma_tile<D, true, false>(src, L, wave, key0, key_end, Kst, Vst);
+}
+
+// Scores of one tile for one wave, then the online softmax with a lazy
+// rescale: the running max only moves (and O, l are rescaled) when some row
+// of the wave sees a score more than 2^8 above it; otherwise p = 2^(s*c - m)
+// stays below 256, which bf16 P and fp32 O, l hold exactly as well as
+// smaller values. The result is the same softmax; only the reference point
+// of the exponent differs between rescales.
+template <int D, bool MASK>
+__device__ __forceinline__ void dma_compute(const char* Kst, const char* Vst, const DmaLane<D>& L,
+                                            State<DmaCfg<D>>& s, int kpos0, int n_valid, int causal,
+                                            int row_pos, float c, int i, int h) {
+  using C = DmaCfg<D>;
+  constexpr float kTau = 8.f;
+  f32x16_t sacc[C::SB];
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8_t av =
+          *(const bf16x8_t*)(Kst + kb * 32 * C::ROW + L.kaddr[ks & 3] + (ks >> 2) * 128);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s.qf[ks], sacc[kb], 0, 0, 0);
+    }
+  }
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < C::SB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kl = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool vis = kl < n_valid && (!causal || kpos0 + kl <= row_pos);
+        sacc[kb][r] = vis ? sacc[kb][r] : kNegInf;
+      }
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  if (__builtin_amdgcn_ballot_w64(mx > s.m + kTau) != 0) {
+    const float m_new = __builtin_fmaxf(s.m, mx);
+    const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(s.m - m_new);
+    s.l *= corr;
+#pragma unroll
+    for (int db = 0; db < C::OB; ++db) s.o[db] *= corr;
+    s.m = m_new;
+  }
+  const float m_use = (s.m == kNegInf) ? 0.f : s.m;
+  float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -m_use));
+      const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
+      sacc[kb][r] = p0;
+      sacc[kb][r + 1] = p1;
+      rs0 += p0;
+      rs1 += p1;
+    }
+  float rs = rs0 + rs1;
+  s.l += rs + __shfl_xor(rs, 32);
+#pragma unroll
+  for (int kb = 0; kb < C::SB; ++kb)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * cc + e];
+      const int krow = (16 * (2 * kb + cc)) * C::ROW;
+#pragma unroll
+      for (int db = 0; db < C::OB; ++db) {
+        const char* vb = Vst + krow + L.vaddr[db & 1] + (db >> 1) * 128;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(vb));
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(vb + 8 * C::ROW));
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        s.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, s.o[db], 0, 0, 0);
+      }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_step(const char* Kst, const char* Vst, const DmaLane<D>& L,
+                                         State<DmaCfg<D>>& s, const UnitDesc& u, int tk0, int key_end,
+                                         int causal, int row_pos, int pmin, int pmax, bool active, float c,
+                                         int i, int h) {
+  using C = DmaCfg<D>;
+  const int kpos0 = u.key_pos0 + tk0;
+  if (!active || (causal && kpos0 > pmax)) return;   // no rows, or the tile is all-future for the wave
+  const int nvalid = min(C::BN, key_end - tk0);
+  const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
+  if (need_mask) dma_compute<D, true>(Kst, Vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  else dma_compute<D, false>(Kst, Vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
+}
+
+template <int D>
+__global__ void __launch_bounds__(512, 2)
+attn_wide_dma(AttnArgs a) {
+  using C = DmaCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char v0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char k1[C::TB];
+  __shared__ __attribute__((aligned(1024))) char v1[C::TB];
+  __shared__ __attribute__((aligned(1024))) char k2[C::TB];
+  __shared__ __attribute__((aligned(1024))) char v2[C::TB];
+  const WorkItem it = a.items[blockIdx.x];
+  const UnitDesc u = a.units[it.unit];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
+  const int rloc = wave * 32 + i;
+  const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
+  State<C> s;
+  load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+  int pmin, pmax;
+  wave_pos_range(w, &pmin, &pmax);
+  const bool active = wave * 32 < it.n_rows;
+  const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+  const DmaLane<D> L = dma_lane<D>(wave, lane);
+  const float c = a.scale_log2;
+  const int kb0 = it.key_begin, ke = it.key_end;
+  const int nt = (ke - kb0 + C::BN - 1) / C::BN;
+
+  dma_tile_any<D>(src, L, wave, kb0, ke, k0, v0);
+  if (nt > 1) dma_tile_any<D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
+#define GQA_DMA_STEP(KS, VS, KN, VN)                                                              \
+  {                                                                                               \
+    if (j + 1 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::VM_PER_TILE));                \
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                         \
+    __builtin_amdgcn_s_barrier();                                                                 \
+    if (j + 2 < nt) dma_tile_any<D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN, VN);            \
+    dma_step<D>(KS, VS, L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax, active, c, i, h); \
+  }
+  for (int j0 = 0; j0 < nt; j0 += 3) {
+    {
+      const int j = j0;
+      GQA_DMA_STEP(k0, v0, k2, v2)
+    }
+    if (j0 + 1 < nt) {
+      const int j = j0 + 1;
+      GQA_DMA_STEP(k1, v1, k0, v0)
+    }
+    if (j0 + 2 < nt) {
+      const int j = j0 + 2;
+      GQA_DMA_STEP(k2, v2, k1, v1)
+    }
+  }
+#undef GQA_DMA_STEP
+  write_row<C, uint16_t, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
+}
+
 // -------------------------------------------------------------- narrow ----
 template <typename T, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, (Cfg<T, D, true>::WAVES_PER_SIMD))
 attn_narrow(AttnArgs a) {
   using C = Cfg<T, D, true>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -478,30 +827,26 @@ attn_narrow(AttnArgs a) {
   load_q<C, T, D>(a, w, it.kv, h, s);
   int pmin, pmax;
   wave_pos_range(w, &pmin, &pmax);
+  const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
 
-  const int nkeys = it.key_end - it.key_begin;
-  const int nt = (nkeys + C::BN - 1) / C::BN;   // wave tiles; wave w takes w, w+4, ...
+  const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;   // wave tiles: wave w takes w, w+4, ...
   const int rounds = (nt + 3) / 4;
   char* stg = smem + wave * C::STAGE;
   T* Ks = (T*)stg;
   T* Vs = (T*)(stg + C::K_ELEMS * sizeof(T));
   Stage<C> st;
-  if (wave < nt) load_tile<C, T, D>(a, u, it.kv, it.key_begin + wave * C::BN, it.key_end, lane, st);
+  if (wave < nt) load_tile<C, T, D>(src, it.key_begin + wave * C::BN, it.key_end, lane, st);
   for (int rd = 0; rd < rounds; ++rd) {
     const int j = wave + 4 * rd;
     const bool have = j < nt;
     if (have) store_tile<C, T, D>(Ks, Vs, lane, st);
     __syncthreads();
-    if (j + 4 < nt) load_tile<C, T, D>(a, u, it.kv, it.key_begin + (j + 4) * C::BN, it.key_end, lane, st);
+    if (j + 4 < nt) load_tile<C, T, D>(src, it.key_begin + (j + 4) * C::BN, it.key_end, lane, st);
     if (have) {
       const int tk0 = it.key_begin + j * C::BN;
-      const int nvalid = min(C::BN, it.key_end - tk0);
       const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
-      if (!future) {
-        const bool need_mask = (nvalid < C::BN) || (a.causal && u.key_pos0 + tk0 + C::BN - 1 > pmin);
-        compute_tile<C, T, D>(Ks, Vs, s, tk0, nvalid, need_mask, a.causal, u.key_pos0, w.pos,
-                              a.scale_log2, i, h);
-      }
+      if (!future)
+        run_tile<C, T, D>(Ks, Vs, s, u, tk0, it.key_end, a.causal, w.pos, pmin, a.scale_log2, i, h);
     }
     __syncthreads();
   }
@@ -545,15 +890,17 @@ attn_narrow(AttnArgs a) {
 
 // --------------------------------------------------------------- merge ----
 // One workgroup per (query token, KV head); each thread owns 4 consecutive
-// d values of one of the G rows. Partials are combined in a fixed order
-// (prefix shards, then suffix shards), so the result is bitwise repeatable
-// (ADR-0060 GQA fused attention, §4: m = max m_i, weights exp(m_i - m),
-// normalise once at the end).
+// d values of one of the G rows. Partials are folded in a fixed order
+// (prefix shards, then suffix shards) with the same online rule as the
+// tile loop, so the result is bitwise repeatable (ADR-0060 GQA fused
+// attention, §4: m = max m_i, weights exp(m_i - m), normalise once at the
+// end). Loads of several partials are issued before they are consumed.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 lse_merge(AttnArgs a) {
   const int tok = blockIdx.x / a.H_kv, kv = blockIdx.x - tok * a.H_kv;
   constexpr int TPR = D / 4;   // threads per row
+  constexpr int U = 4;         // partials in flight per thread
   const int b = branch_of(a.branches, 0, a.n_branches, tok);
   const BranchDesc br = a.branches[b];
   for (int g = threadIdx.x / TPR; g < a.G; g += 256 / TPR) {
@@ -568,33 +915,48 @@ lse_merge(AttnArgs a) {
       live[1] = unit_live(a, br.unit_pr, tok, g, kv, &base[1]);
       bm[1] = a.units[br.unit_pr].bm;
     }
-    if (live[0] + live[1] < 2) continue;   // written directly by the attention kernel
-    float M = kNegInf;
-    for (int x = 0; x < 2; ++x)
-      for (int sI = 0; sI < live[x]; ++sI) M = fmaxf(M, a.part_ml[base[x] + (int64_t)sI * bm[x]].x);
-    const float M_use = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    for (int x = 0; x < 2; ++x)
-      for (int sI = 0; sI < live[x]; ++sI) {
-        const int64_t p = base[x] + (int64_t)sI * bm[x];
-        const float2 ml = a.part_ml[p];
-        const float wgt = exp2_fast(ml.x - M_use);
-        L += ml.y * wgt;
-        const float4 v = *(const float4*)(a.part_o + p * D + d0);
-        o0 += wgt * v.x;
-        o1 += wgt * v.y;
-        o2 += wgt * v.z;
-        o3 += wgt * v.w;
+    const int n = live[0] + live[1];
+    if (n < 2) continue;   // written directly by the attention kernel
+    float M = kNegInf, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q0 = 0; q0 < n; q0 += U) {
+      float2 ml[U];
+      float4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int q = q0 + k;
+        if (q < n) {
+          const int64_t p = (q < live[0]) ? base[0] + (int64_t)q * bm[0]
+                                          : base[1] + (int64_t)(q - live[0]) * bm[1];
+          ml[k] = a.part_ml[p];
+          v[k] = *(const float4*)(a.part_o + p * D + d0);
+        } else {
+          ml[k] = make_float2(kNegInf, 0.f);
+          v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const float Mn = fmaxf(M, ml[k].x);
+        const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+        const float sa = exp2_fast(M - Mu), sb = exp2_fast(ml[k].x - Mu);
+        L = L * sa + ml[k].y * sb;
+        O.x = O.x * sa + v[k].x * sb;
+        O.y = O.y * sa + v[k].y * sb;
+        O.z = O.z * sa + v[k].z * sb;
+        O.w = O.w * sa + v[k].w * sb;
+        M = Mn;
+      }
+    }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     const int64_t orow = ((int64_t)tok * a.H_q + kv * a.G + g);
     if constexpr (std::is_same<T, uint16_t>::value) {
       uint2 pk;
-      pk.x = pack_bf16x2(o0 * inv, o1 * inv);
-      pk.y = pack_bf16x2(o2 * inv, o3 * inv);
+      pk.x = pack_bf16x2(O.x * inv, O.y * inv);
+      pk.y = pack_bf16x2(O.z * inv, O.w * inv);
       *(uint2*)((uint16_t*)a.o + orow * D + d0) = pk;
     } else {
-      *(float4*)((float*)a.o + orow * D + d0) = make_float4(o0 * inv, o1 * inv, o2 * inv, o3 * inv);
+      *(float4*)((float*)a.o + orow * D + d0) = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
     }
     if (d0 == 0) a.lse[orow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
@@ -604,6 +966,8 @@ template <typename T, int D>
 hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
   if (narrow) hipLaunchKernelGGL((attn_narrow<T, D>), dim3(n_items), dim3(256), 0, st, a);
+  else if constexpr (std::is_same<T, uint16_t>::value)
+    hipLaunchKernelGGL((attn_wide_dma<D>), dim3(n_items), dim3(512), 0, st, a);
   else hipLaunchKernelGGL((attn_wide<T, D>), dim3(n_items), dim3(256), 0, st, a);
   return hipGetLastError();
 }

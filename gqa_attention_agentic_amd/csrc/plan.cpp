@@ -105,6 +105,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   *P = Plan();
   const int32_t G = in.H_q / in.H_kv;
   const int32_t ng = (int32_t)in.g_start.size(), nb = (int32_t)in.b_group.size();
+  const int32_t wide_rows = (in.dtype == 0) ? kWideRowsBf16 : kWideRows;
 
   // Branches: token ranges and context lengths; per-token positions (host only).
   P->branches.resize(nb);
@@ -174,7 +175,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
     const int64_t M = (int64_t)u.n_tok * G;
-    u.bm = (M <= kNarrowRows) ? kNarrowRows : kWideRows;
+    u.bm = (M <= kNarrowRows) ? kNarrowRows : wide_rows;
     const int32_t ntile = (int32_t)ceil_div(M, u.bm);
     uw[ui].unit = ui;
     uw[ui].tile_key_end.resize(ntile);
@@ -198,7 +199,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   // stream into about one item per resident workgroup slot, no shard below
   // 256 keys, so every slot streams a similar number of bytes (ADR-0060,
   // §5.2-§5.3: decode is bound by KV loads).
-  const int64_t slots = 2LL * in.n_cu;
+  const int64_t slots = 2LL * in.n_cu;                              // narrow: 2 workgroups per CU
+  const int64_t wide_slots = (in.dtype == 0 ? 1LL : 2LL) * in.n_cu;  // bf16 wide: one 8-wave workgroup per CU
   {
     int64_t wn = 0;
     for (int32_t ui = 0; ui < nu; ++ui)
@@ -217,7 +219,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     std::vector<int32_t> wide_auto;
     int32_t maxlen = 0;
     for (int32_t ui = 0; ui < nu; ++ui)
-      if (P->units[ui].bm == kWideRows && override_of(ui) == 0) {
+      if (P->units[ui].bm != kNarrowRows && override_of(ui) == 0) {
         wide_auto.push_back(ui);
         maxlen = std::max(maxlen, P->units[ui].key_len);
       }
@@ -252,7 +254,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
             if (live > 1) partial_rows += (double)live * rows * in.H_kv;
           }
         }
-        const double total = lpt_makespan(cost, (int)slots) + merge_per_row * partial_rows;
+        const double total = lpt_makespan(cost, (int)wide_slots) + merge_per_row * partial_rows;
         if (total < best * 0.999) {
           best = total;
           best_chunk = chunk;
@@ -270,7 +272,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   int64_t part = 0;
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
-    const int32_t tile_keys = (u.bm == kWideRows) ? kWideKeys : kNarrowKeys;
+    const int32_t tile_keys = (u.bm != kNarrowRows) ? kWideKeys : kNarrowKeys;
     std::vector<int32_t> bnd = shard_bounds(u.key_len, S[ui], tile_keys);
     u.n_splits = (int32_t)bnd.size() - 1;
     P->api_splits[api_slot[ui]] = u.n_splits;
@@ -300,7 +302,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           w.split = s;
           w.tile = (int32_t)t;
           P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
-          (u.bm == kWideRows ? P->wide : P->narrow).push_back(w);
+          (u.bm != kNarrowRows ? P->wide : P->narrow).push_back(w);
         }
       }
     }

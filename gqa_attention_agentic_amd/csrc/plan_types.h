@@ -18,7 +18,8 @@
 
 namespace gqa {
 
-constexpr int kWideRows = 128;    // rows per M-tile of the MFMA-bound kernel (4 waves x 32)
+constexpr int kWideRows = 128;    // rows per M-tile of the fp32 MFMA kernel (4 waves x 32)
+constexpr int kWideRowsBf16 = 256;  // rows per M-tile of the bf16 MFMA kernel (8 waves x 32)
 constexpr int kNarrowRows = 32;   // rows per M-tile of the KV-bandwidth-bound kernel
 constexpr int kWideKeys = 64;     // keys per KV tile, wide kernel
 constexpr int kNarrowKeys = 32;   // keys per KV tile and wave, narrow kernel

@@ -125,22 +125,27 @@ def test_config_split_counts():
     assert _plan(get_config(4))[1] == [8, 0]
 
 
-def test_causal_skip_counts_lower_triangle():
+@pytest.mark.parametrize("dtype,rows", [("bf16", 256), ("fp32", 128)])
+def test_causal_skip_counts_lower_triangle(dtype, rows):
     """Prefill: processed KV tiles equal the lower-triangular tile count (per
-    M-tile of 16 tokens x 8 heads = 128 rows, 64-key tiles, shards of 4096)."""
-    w = custom("tri", H_q=64, H_kv=8, shared=(32768,), branches=((0, 32768, 0),), seed=1, splits=[8, 0])
+    M-tile of rows / G tokens x G heads, 64-key tiles, shards of 4096); the
+    bf16 MFMA kernel uses 256-row M-tiles, the fp32 one 128-row M-tiles."""
+    w = custom("tri", H_q=64, H_kv=8, shared=(32768,), branches=((0, 32768, 0),), seed=1, splits=[8, 0],
+               dtype=dtype)
     items, _, stats = _plan(w)
-    expect = 0
-    for i in range(2048):                     # M-tiles of 16 tokens
-        kend = 16 * i + 16                     # keys visible to the tile's last row
+    tok = rows // 8
+    expect, n_items = 0, 0
+    for i in range(32768 // tok):
+        kend = tok * i + tok                   # keys visible to the tile's last row
         for s in range(8):
             k0, k1 = 4096 * s, min(4096 * (s + 1), kend)
             if k0 < kend:
                 expect += -(-(k1 - k0) // 64)
+                n_items += 8
     assert stats["n_kv_tiles"] == expect * 8
-    assert len(items) == 73728
-    # without the causal clamp the grid would be 2048 * 8 shards * 8 heads * 64 tiles
-    assert stats["n_kv_tiles"] < 2048 * 8 * 8 * 64 * 0.51
+    assert len(items) == n_items
+    # without the causal clamp the grid would be (M-tiles) * 8 shards * 8 heads * 64 tiles
+    assert stats["n_kv_tiles"] < (32768 // tok) * 8 * 8 * 64 * 0.52
 
 
 def test_heuristic_fills_the_device():
