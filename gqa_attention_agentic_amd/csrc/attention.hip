@@ -667,13 +667,29 @@ __device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const D
 // of the wave sees a score more than 2^8 above it; otherwise p = 2^(s*c - m)
 // stays below 256, which bf16 P and fp32 O, l hold exactly as well as
 // smaller values. The result is the same softmax; only the reference point
-// of the exponent differs between rescales.
+// of the exponent differs between rescales. The exponentials of each 32-key
+// half are computed right before that half's P.V products, so the second
+// half's VALU work overlaps the first half's MFMAs.
 template <int D, bool MASK>
-__device__ __forceinline__ void dma_compute(const char* Kst, const char* Vst, const DmaLane<D>& L,
+__device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const DmaLane<D>& L,
                                             State<DmaCfg<D>>& s, int kpos0, int n_valid, int causal,
                                             int row_pos, float c, int i, int h) {
   using C = DmaCfg<D>;
   constexpr float kTau = 8.f;
+  typedef __attribute__((address_space(3))) const bf16x8_t* lds_bf16x8;
+  typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16;
+  // Per-call opaque bases: every operand address below is base + immediate.
+  uint32_t kb4[4], vb2[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    kb4[q] = kst + L.kaddr[q];
+    asm volatile("" : "+v"(kb4[q]));
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    vb2[q] = vst + L.vaddr[q];
+    asm volatile("" : "+v"(vb2[q]));
+  }
   f32x16_t sacc[C::SB];
 #pragma unroll
   for (int kb = 0; kb < C::SB; ++kb) {
@@ -681,8 +697,7 @@ __device__ __forceinline__ void dma_compute(const char* Kst, const char* Vst, co
     for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8_t av =
-          *(const bf16x8_t*)(Kst + kb * 32 * C::ROW + L.kaddr[ks & 3] + (ks >> 2) * 128);
+      const bf16x8_t av = *(lds_bf16x8)(uintptr_t)(kb4[ks & 3] + kb * 32 * C::ROW + (ks >> 2) * 128);
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s.qf[ks], sacc[kb], 0, 0, 0);
     }
   }
@@ -710,23 +725,21 @@ __device__ __forceinline__ void dma_compute(const char* Kst, const char* Vst, co
     for (int db = 0; db < C::OB; ++db) s.o[db] *= corr;
     s.m = m_new;
   }
-  const float m_use = (s.m == kNegInf) ? 0.f : s.m;
-  float rs0 = 0.f, rs1 = 0.f;
+  const float neg_m = (s.m == kNegInf) ? 0.f : -s.m;
+  float rs = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < C::SB; ++kb)
+  for (int kb = 0; kb < C::SB; ++kb) {
+    float r0 = 0.f, r1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -m_use));
-      const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, -m_use));
+      const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, neg_m));
+      const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, neg_m));
       sacc[kb][r] = p0;
       sacc[kb][r + 1] = p1;
-      rs0 += p0;
-      rs1 += p1;
+      r0 += p0;
+      r1 += p1;
     }
-  float rs = rs0 + rs1;
-  s.l += rs + __shfl_xor(rs, 32);
-#pragma unroll
-  for (int kb = 0; kb < C::SB; ++kb)
+    rs += r0 + r1;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       bf16x8_t pb;
@@ -735,30 +748,39 @@ __device__ __forceinline__ void dma_compute(const char* Kst, const char* Vst, co
       const int krow = (16 * (2 * kb + cc)) * C::ROW;
 #pragma unroll
       for (int db = 0; db < C::OB; ++db) {
-        const char* vb = Vst + krow + L.vaddr[db & 1] + (db >> 1) * 128;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(vb));
-        const v4i16_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(vb + 8 * C::ROW));
+        const uint32_t va = vb2[db & 1] + krow + (db >> 1) * 128;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)va);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)(va + 8 * C::ROW));
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         s.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, s.o[db], 0, 0, 0);
       }
     }
+  }
+  s.l += rs + __shfl_xor(rs, 32);
 }
 
 template <int D>
-__device__ __forceinline__ void dma_step(const char* Kst, const char* Vst, const DmaLane<D>& L,
-                                         State<DmaCfg<D>>& s, const UnitDesc& u, int tk0, int key_end,
-                                         int causal, int row_pos, int pmin, int pmax, bool active, float c,
-                                         int i, int h) {
+__device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLane<D>& L, State<DmaCfg<D>>& s,
+                                         const UnitDesc& u, int tk0, int key_end, int causal, int row_pos,
+                                         int pmin, int pmax, bool active, float c, int i, int h) {
   using C = DmaCfg<D>;
   const int kpos0 = u.key_pos0 + tk0;
   if (!active || (causal && kpos0 > pmax)) return;   // no rows, or the tile is all-future for the wave
   const int nvalid = min(C::BN, key_end - tk0);
   const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
-  if (need_mask) dma_compute<D, true>(Kst, Vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
-  else dma_compute<D, false>(Kst, Vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  if (need_mask) dma_compute<D, true>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  else dma_compute<D, false>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
 }
 
+__device__ __forceinline__ uint32_t lds_u32(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Four ring stages consumed two tiles per barrier: after the barrier of pair
+// p (tiles 2p, 2p+1) the DMA of pair p+1 is issued into the two stages the
+// previous pair used, then pair p is computed, so loads run two tiles ahead
+// and the waves sharing a SIMD may drift apart by up to a tile between
+// barriers.
 template <int D>
 __global__ void __launch_bounds__(512, 2)
 attn_wide_dma(AttnArgs a) {
@@ -769,6 +791,8 @@ attn_wide_dma(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char v1[C::TB];
   __shared__ __attribute__((aligned(1024))) char k2[C::TB];
   __shared__ __attribute__((aligned(1024))) char v2[C::TB];
+  __shared__ __attribute__((aligned(1024))) char k3[C::TB];
+  __shared__ __attribute__((aligned(1024))) char v3[C::TB];
   const WorkItem it = a.items[blockIdx.x];
   const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
@@ -787,29 +811,29 @@ attn_wide_dma(AttnArgs a) {
 
   dma_tile_any<D>(src, L, wave, kb0, ke, k0, v0);
   if (nt > 1) dma_tile_any<D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
-#define GQA_DMA_STEP(KS, VS, KN, VN)                                                              \
-  {                                                                                               \
-    if (j + 1 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::VM_PER_TILE));                \
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                         \
-    __builtin_amdgcn_s_barrier();                                                                 \
-    if (j + 2 < nt) dma_tile_any<D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN, VN);            \
-    dma_step<D>(KS, VS, L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax, active, c, i, h); \
+#define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                              \
+  {                                                                                                   \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                                  \
+    __builtin_amdgcn_s_barrier();                                                                     \
+    if (j + 2 < nt) dma_tile_any<D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);              \
+    if (j + 3 < nt) dma_tile_any<D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);              \
+    dma_step<D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,  \
+                active, c, i, h);                                                                     \
+    if (j + 1 < nt)                                                                                   \
+      dma_step<D>(lds_u32(KB), lds_u32(VB), L, s, u, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin, \
+                  pmax, active, c, i, h);                                                             \
   }
-  for (int j0 = 0; j0 < nt; j0 += 3) {
+  for (int j0 = 0; j0 < nt; j0 += 4) {
     {
       const int j = j0;
-      GQA_DMA_STEP(k0, v0, k2, v2)
-    }
-    if (j0 + 1 < nt) {
-      const int j = j0 + 1;
-      GQA_DMA_STEP(k1, v1, k0, v0)
+      GQA_DMA_PAIR(k0, v0, k1, v1, k2, v2, k3, v3)
     }
     if (j0 + 2 < nt) {
       const int j = j0 + 2;
-      GQA_DMA_STEP(k2, v2, k1, v1)
+      GQA_DMA_PAIR(k2, v2, k3, v3, k0, v0, k1, v1)
     }
   }
-#undef GQA_DMA_STEP
+#undef GQA_DMA_PAIR
   write_row<C, uint16_t, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
 }
 
