@@ -62,7 +62,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("GQA_ATTN_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m gqa_attention_agentic_amd.build`")
     lib = ctypes.CDLL(p)

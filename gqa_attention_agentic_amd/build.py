@@ -35,7 +35,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP extension)")
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
+def build(verbose: bool = False, resource_usage: bool = False, defines=(), lib_path: str = LIB) -> str:
     cc = hipcc()
     objs = []
     bdir = os.path.join(HERE, "_build")
@@ -44,8 +44,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
               f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(bdir, src + ".o")
-        cmd = [cc] + common + NO_PACKED_FP32
+        obj = os.path.join(bdir, src + ("." + "_".join(defines) if defines else "") + ".o")
+        cmd = [cc] + common + NO_PACKED_FP32 + [f"-D{d}" for d in defines]
         if src.endswith(".hip"):
             cmd += KERNEL_FP
         if src.endswith(".hip") and resource_usage:
@@ -61,15 +61,15 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         if out.strip() and (verbose or resource_usage):
             print(out, flush=True)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

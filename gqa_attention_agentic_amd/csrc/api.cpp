@@ -370,7 +370,7 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   if (tm) tm->merged = Q.merge_rows > 0;
   if (Q.merge_rows > 0) {
     if (tm) hipEventRecord(tm->ev[2], st);
-    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, st);
+    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, Q.max_row_parts, st);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     if (tm) hipEventRecord(tm->ev[3], st);
   }

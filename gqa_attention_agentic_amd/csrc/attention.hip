@@ -580,20 +580,19 @@ constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 #define GQA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int D>
+template <class C>
 struct DmaLane {
   // per-lane constants of the DMA (global side) and of the operand reads (LDS side)
-  int key_rel[DmaCfg<D>::PER_WAVE];   // tile-relative key of this lane's chunk in instruction q
-  int colK[DmaCfg<D>::PER_WAVE];      // element offset inside the key row (logical chunk * 8)
-  int colV[DmaCfg<D>::PER_WAVE];
+  int key_rel[C::PER_WAVE];   // tile-relative key of this lane's chunk in instruction q
+  int colK[C::PER_WAVE];      // element offset inside the key row (logical chunk * 8)
+  int colV[C::PER_WAVE];
   int kaddr[4];                       // byte offset of K operand chunk for ks = 0..3 (ks+4: +128)
   int vaddr[2];                       // byte offset of the V tr16 read for db = 0, 1 (db+2: +128)
 };
 
-template <int D>
-__device__ __forceinline__ DmaLane<D> dma_lane(int wave, int lane) {
-  using C = DmaCfg<D>;
-  DmaLane<D> L;
+template <class C>
+__device__ __forceinline__ DmaLane<C> dma_lane(int wave, int lane) {
+  DmaLane<C> L;
 #pragma unroll
   for (int q = 0; q < C::PER_WAVE; ++q) {
     const int byte = (wave * C::PER_WAVE + q) * 1024 + 16 * lane;
@@ -619,10 +618,9 @@ __device__ __forceinline__ DmaLane<D> dma_lane(int wave, int lane) {
 // later). Paged sources with power-of-two pages of >= 16 tokens read the
 // tile's page ids with scalar loads, so no vector-memory wait is needed
 // before the addresses are formed.
-template <int D, bool PAGED, bool SCALAR_PAGES>
-__device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLane<D>& L, int wave, int key0,
+template <class C, int D, bool PAGED, bool SCALAR_PAGES>
+__device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLane<C>& L, int wave, int key0,
                                          int key_end, char* Kst, char* Vst) {
-  using C = DmaCfg<D>;
   int pg[5] = {0, 0, 0, 0, 0};
   int lp0 = 0;
   if (PAGED && SCALAR_PAGES) {
@@ -654,12 +652,12 @@ __device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLa
   }
 }
 
-template <int D>
-__device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const DmaLane<D>& L, int wave, int key0,
+template <class C, int D>
+__device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const DmaLane<C>& L, int wave, int key0,
                                              int key_end, char* Kst, char* Vst) {
-  if (!src.paged) dma_tile<D, false, false>(src, L, wave, key0, key_end, Kst, Vst);
-  else if (src.shift >= 4) dma_tile<D, true, true>(src, L, wave, key0, key_end, Kst, Vst);
-  else dma_tile<D, true, false>(src, L, wave, key0, key_end, Kst, Vst);
+  if (!src.paged) dma_tile<C, D, false, false>(src, L, wave, key0, key_end, Kst, Vst);
+  else if (src.shift >= 4) dma_tile<C, D, true, true>(src, L, wave, key0, key_end, Kst, Vst);
+  else dma_tile<C, D, true, false>(src, L, wave, key0, key_end, Kst, Vst);
 }
 
 // Scores of one tile for one wave, then the online softmax with a lazy
@@ -670,11 +668,10 @@ __device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const D
 // of the exponent differs between rescales. The exponentials of each 32-key
 // half are computed right before that half's P.V products, so the second
 // half's VALU work overlaps the first half's MFMAs.
-template <int D, bool MASK>
-__device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const DmaLane<D>& L,
-                                            State<DmaCfg<D>>& s, int kpos0, int n_valid, int causal,
+template <class C, int D, bool MASK>
+__device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const DmaLane<C>& L,
+                                            State<C>& s, int kpos0, int n_valid, int causal,
                                             int row_pos, float c, int i, int h) {
-  using C = DmaCfg<D>;
   constexpr float kTau = 8.f;
   typedef __attribute__((address_space(3))) const bf16x8_t* lds_bf16x8;
   typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16;
@@ -759,17 +756,16 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
   s.l += rs + __shfl_xor(rs, 32);
 }
 
-template <int D>
-__device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLane<D>& L, State<DmaCfg<D>>& s,
+template <class C, int D>
+__device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLane<C>& L, State<C>& s,
                                          const UnitDesc& u, int tk0, int key_end, int causal, int row_pos,
                                          int pmin, int pmax, bool active, float c, int i, int h) {
-  using C = DmaCfg<D>;
   const int kpos0 = u.key_pos0 + tk0;
   if (!active || (causal && kpos0 > pmax)) return;   // no rows, or the tile is all-future for the wave
   const int nvalid = min(C::BN, key_end - tk0);
   const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
-  if (need_mask) dma_compute<D, true>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
-  else dma_compute<D, false>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  if (need_mask) dma_compute<C, D, true>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  else dma_compute<C, D, false>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const char* p) {
@@ -804,23 +800,23 @@ attn_wide_dma(AttnArgs a) {
   wave_pos_range(w, &pmin, &pmax);
   const bool active = wave * 32 < it.n_rows;
   const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
-  const DmaLane<D> L = dma_lane<D>(wave, lane);
+  const DmaLane<C> L = dma_lane<C>(wave, lane);
   const float c = a.scale_log2;
   const int kb0 = it.key_begin, ke = it.key_end;
   const int nt = (ke - kb0 + C::BN - 1) / C::BN;
 
-  dma_tile_any<D>(src, L, wave, kb0, ke, k0, v0);
-  if (nt > 1) dma_tile_any<D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
+  dma_tile_any<C, D>(src, L, wave, kb0, ke, k0, v0);
+  if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
 #define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                              \
   {                                                                                                   \
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                                  \
     __builtin_amdgcn_s_barrier();                                                                     \
-    if (j + 2 < nt) dma_tile_any<D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);              \
-    if (j + 3 < nt) dma_tile_any<D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);              \
-    dma_step<D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,  \
+    if (j + 2 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);              \
+    if (j + 3 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);              \
+    dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,  \
                 active, c, i, h);                                                                     \
     if (j + 1 < nt)                                                                                   \
-      dma_step<D>(lds_u32(KB), lds_u32(VB), L, s, u, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin, \
+      dma_step<C, D>(lds_u32(KB), lds_u32(VB), L, s, u, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin, \
                   pmax, active, c, i, h);                                                             \
   }
   for (int j0 = 0; j0 < nt; j0 += 4) {
@@ -912,6 +908,114 @@ attn_narrow(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------- narrow, bf16, DMA ----
+// KV-bandwidth-bound items (<= 32 rows, decode): each of the 4 waves streams
+// its own 32-key tiles (wave w takes tiles w, w+4, ...) through a private
+// 2-stage LDS ring filled by global->LDS DMA, with no barrier inside the
+// loop; for an item of up to 8 tiles every byte of its shard is requested at
+// kernel start. The four per-wave (m, l, O) states are merged through LDS at
+// the end. Same LDS swizzles, operand reads and softmax as the wide kernel.
+template <int D>
+struct NarrowDmaCfg {
+  static constexpr bool BF16 = true;
+  static constexpr int BM = kNarrowRows;
+  static constexpr int BN = 32;                     // keys per wave tile
+  static constexpr int ROW = D * 2;
+  static constexpr int TB = BN * ROW;               // bytes per tensor per tile
+  static constexpr int NINST = TB / 1024;           // 1 KB DMA instructions per tensor per tile
+  static constexpr int PER_WAVE = NINST;            // each wave issues its whole tile
+  static constexpr int OB = D / 32, QF = D / 16, SB = BN / 32;
+  static constexpr int MERGE_O = 4 * OB * 16 * 64 * 4;   // bytes of the per-wave O^T exchange
+  static_assert(4 * 2 * TB >= MERGE_O, "stage-0 ring must hold the merge exchange");
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 1)
+attn_narrow_dma(AttnArgs a) {
+  using C = NarrowDmaCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char st0[4 * 2 * C::TB];   // per wave: K tile then V tile
+  __shared__ __attribute__((aligned(1024))) char st1[4 * 2 * C::TB];
+  const WorkItem it = a.items[blockIdx.x];
+  const UnitDesc u = a.units[it.unit];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
+  const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+  State<C> s;
+  load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+  int pmin, pmax;
+  wave_pos_range(w, &pmin, &pmax);
+  const bool active = it.n_rows > 0;
+  const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+  const DmaLane<C> L = dma_lane<C>(0, lane);
+  const float c = a.scale_log2;
+  const int kb0 = it.key_begin, ke = it.key_end, causal = a.causal;
+  const int nt = (ke - kb0 + C::BN - 1) / C::BN;
+  constexpr int VM = 2 * C::NINST;
+  char* K0 = st0 + wave * 2 * C::TB;
+  char* V0 = K0 + C::TB;
+  char* K1 = st1 + wave * 2 * C::TB;
+  char* V1 = K1 + C::TB;
+  if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
+  if (wave + 4 < nt) dma_tile_any<C, D>(src, L, 0, kb0 + (wave + 4) * C::BN, ke, K1, V1);
+  for (int j = wave; j < nt; j += 8) {
+    if (j + 4 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, u, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
+                   i, h);
+    if (j + 8 < nt) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));   // own LDS reads of stage 0 done
+      dma_tile_any<C, D>(src, L, 0, kb0 + (j + 8) * C::BN, ke, K0, V0);
+    }
+    const int j2 = j + 4;
+    if (j2 >= nt) break;
+    if (j2 + 4 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    dma_step<C, D>(lds_u32(K1), lds_u32(V1), L, s, u, kb0 + j2 * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
+                   i, h);
+    if (j2 + 8 < nt) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+      dma_tile_any<C, D>(src, L, 0, kb0 + (j2 + 8) * C::BN, ke, K1, V1);
+    }
+  }
+  // Merge the four waves' states (same rows, disjoint keys) through LDS.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __syncthreads();
+  float* mo = (float*)st0;                       // [wave][db][r][lane]
+  float2* mml = (float2*)st1;
+#pragma unroll
+  for (int db = 0; db < C::OB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
+  mml[wave * 64 + lane] = make_float2(s.m, s.l);
+  __syncthreads();
+  float mk[4], lk[4];
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float2 x = mml[k * 64 + lane];
+    mk[k] = x.x;
+    lk[k] = x.y;
+    M = fmaxf(M, x.x);
+  }
+  const float M_use = (M == kNegInf) ? 0.f : M;
+  float Lsum = 0.f, wk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    wk[k] = exp2_fast(mk[k] - M_use);
+    Lsum += lk[k] * wk[k];
+  }
+  for (int db = wave; db < C::OB; db += 4) {
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
+      acc[r] = x;
+    }
+    write_row<C, uint16_t, D>(a, it, u, w, M, Lsum, &acc, db, db + 1, wave == 0, h);
+  }
+}
+
 // --------------------------------------------------------------- merge ----
 // One workgroup per (query token, KV head); each thread owns 4 consecutive
 // d values of one of the G rows. Partials are folded in a fixed order
@@ -919,12 +1023,11 @@ attn_narrow(AttnArgs a) {
 // tile loop, so the result is bitwise repeatable (ADR-0060 GQA fused
 // attention, §4: m = max m_i, weights exp(m_i - m), normalise once at the
 // end). Loads of several partials are issued before they are consumed.
-template <typename T, int D>
+template <typename T, int D, int U>
 __global__ void __launch_bounds__(256)
 lse_merge(AttnArgs a) {
   const int tok = blockIdx.x / a.H_kv, kv = blockIdx.x - tok * a.H_kv;
   constexpr int TPR = D / 4;   // threads per row
-  constexpr int U = 4;         // partials in flight per thread
   const int b = branch_of(a.branches, 0, a.n_branches, tok);
   const BranchDesc br = a.branches[b];
   for (int g = threadIdx.x / TPR; g < a.G; g += 256 / TPR) {
@@ -989,18 +1092,26 @@ lse_merge(AttnArgs a) {
 template <typename T, int D>
 hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStream_t st) {
   if (n_items <= 0) return hipSuccess;
-  if (narrow) hipLaunchKernelGGL((attn_narrow<T, D>), dim3(n_items), dim3(256), 0, st, a);
-  else if constexpr (std::is_same<T, uint16_t>::value)
+  if (narrow) {
+    if constexpr (std::is_same<T, uint16_t>::value)
+      hipLaunchKernelGGL((attn_narrow_dma<D>), dim3(n_items), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_narrow<T, D>), dim3(n_items), dim3(256), 0, st, a);
+  } else if constexpr (std::is_same<T, uint16_t>::value)
     hipLaunchKernelGGL((attn_wide_dma<D>), dim3(n_items), dim3(512), 0, st, a);
   else hipLaunchKernelGGL((attn_wide<T, D>), dim3(n_items), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
+// U = partials whose loads a thread issues before folding them: as many as
+// the largest row needs (up to 16), fewer when rows have few partials so the
+// kernel keeps its occupancy.
 template <typename T, int D>
-hipError_t launch_merge_t(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_merge_t(const AttnArgs& a, int max_parts, hipStream_t st) {
   const int64_t blocks = (int64_t)a.n_q_tokens * a.H_kv;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((lse_merge<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (max_parts <= 4) hipLaunchKernelGGL((lse_merge<T, D, 4>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else if (max_parts <= 8) hipLaunchKernelGGL((lse_merge<T, D, 8>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((lse_merge<T, D, 16>), dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1016,13 +1127,13 @@ hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int
   return launch_attn_t<float, 64>(a, n_items, narrow, stream);
 }
 
-hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t stream) {
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream) {
   if (dtype == 0) {
-    if (head_dim == 128) return launch_merge_t<uint16_t, 128>(a, stream);
-    return launch_merge_t<uint16_t, 64>(a, stream);
+    if (head_dim == 128) return launch_merge_t<uint16_t, 128>(a, max_parts, stream);
+    return launch_merge_t<uint16_t, 64>(a, max_parts, stream);
   }
-  if (head_dim == 128) return launch_merge_t<float, 128>(a, stream);
-  return launch_merge_t<float, 64>(a, stream);
+  if (head_dim == 128) return launch_merge_t<float, 128>(a, max_parts, stream);
+  return launch_merge_t<float, 64>(a, max_parts, stream);
 }
 
 }  // namespace gqa

@@ -41,6 +41,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int
                             int head_dim, hipStream_t stream);
 
 // Log-sum-exp merge of the partials of every output row with >= 2 of them.
-hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t stream);
+// max_parts: the largest number of partials any output row has.
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream);
 
 }  // namespace gqa

@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdio>
 #include <functional>
@@ -59,6 +60,62 @@ double lpt_makespan(std::vector<double> cost, int slots) {
     mk = std::max(mk, t);
   }
   return mk;
+}
+
+// Workgroups are dealt to the 8 XCDs of the chip round-robin by launch
+// index, and each XCD has its own L2. Items that read the same KV range
+// (same unit, KV head and shard; different M-tiles) are therefore put on
+// launch indices of one residue mod 8, next to each other, so their K/V
+// tiles are fetched into one L2 once. Groups go to the least-loaded XCD,
+// largest first; each XCD's queue keeps the largest-first order.
+constexpr int kXcds = 8;
+
+void xcd_order(std::vector<WorkItem>* items, int n_cu) {
+  if (items->size() < (size_t)2 * kXcds || n_cu % kXcds != 0) return;
+  struct Group { std::vector<WorkItem> v; int64_t cost = 0; };
+  std::vector<Group> groups;
+  {
+    std::vector<std::pair<std::array<int32_t, 3>, size_t>> keyed;
+    std::vector<std::array<int32_t, 3>> keys;
+    for (const WorkItem& w : *items) {
+      const std::array<int32_t, 3> k{w.unit, w.kv, w.split};
+      size_t gi = 0;
+      for (; gi < keys.size(); ++gi)
+        if (keys[gi] == k) break;
+      if (gi == keys.size()) {
+        keys.push_back(k);
+        groups.emplace_back();
+      }
+      groups[gi].v.push_back(w);
+      groups[gi].cost += (int64_t)(w.key_end - w.key_begin) + 96;
+    }
+  }
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group& a, const Group& b) { return a.cost > b.cost; });
+  std::vector<std::vector<WorkItem>> q(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  for (const Group& g : groups) {
+    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    q[x].insert(q[x].end(), g.v.begin(), g.v.end());
+    load[x] += g.cost;
+  }
+  std::vector<size_t> head(kXcds, 0);
+  size_t done = 0;
+  std::vector<WorkItem> out;
+  out.reserve(items->size());
+  while (done < items->size()) {
+    for (int x = 0; x < kXcds && done < items->size(); ++x) {
+      int src = x;
+      if (head[src] == q[src].size()) {   // this XCD's queue ran dry: take from the fullest
+        size_t best = 0;
+        for (int y = 0; y < kXcds; ++y)
+          if (q[y].size() - head[y] > best) { best = q[y].size() - head[y]; src = y; }
+      }
+      out.push_back(q[src][head[src]++]);
+      ++done;
+    }
+  }
+  *items = std::move(out);
 }
 
 }  // namespace
@@ -320,6 +377,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   };
   std::stable_sort(P->wide.begin(), P->wide.end(), by_cost);
   std::stable_sort(P->narrow.begin(), P->narrow.end(), by_cost);
+  xcd_order(&P->wide, in.n_cu);
 
   // Output rows that need the merge kernel (two or more live partials).
   for (int32_t b = 0; b < nb; ++b) {
@@ -335,6 +393,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           n += P->tiles[u.tile_off + r / u.bm].live;
         }
         if (n >= 2) P->merge_rows += in.H_kv;
+        P->max_row_parts = std::max(P->max_row_parts, n);
       }
     }
   }

@@ -35,6 +35,7 @@ struct Plan {
   int64_t part_rows = 0;            // partial rows in the workspace
   int64_t n_kv_tiles = 0;           // (item, KV tile) pairs
   int64_t merge_rows = 0;           // output rows with two or more partials
+  int32_t max_row_parts = 0;        // largest partial count of any output row
   int32_t max_splits = 0;
   int32_t n_q_tokens = 0;
   int32_t n_shared_tokens = 0;
