@@ -577,8 +577,45 @@ struct DmaCfg {
 // s_waitcnt immediate: vmcnt(vm), expcnt(7), lgkmcnt(0).
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
 
+// The DMA below is issued as inline assembly, so the compiler neither counts
+// it nor inserts waits for it (its own tracking of LDS DMA cannot tell ring
+// stages apart and would make every LDS read wait for all DMA in flight).
+// Every consumer waits explicitly with wait_dma<VM>(): at most VM of this
+// thread's vector-memory operations still outstanding (they complete in
+// order) and all its LDS operations done. Both carry a memory clobber, so
+// the compiler moves no LDS access across them.
+template <int VM>
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from gptr into LDS: lane l writes lds_base + 16 l
+// (lds_base wave-uniform, passed in M0; one wait state between the write of
+// M0 and the load).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier that is also a compiler barrier for memory and for the
+// instruction scheduler.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-#define GQA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS byte address of a __shared__ object (or of an LDS pointer).
+__device__ __forceinline__ uint32_t lds_u32(const char* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+__device__ __forceinline__ uint32_t lds_u32(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
 template <class C>
 struct DmaLane {
@@ -618,9 +655,9 @@ __device__ __forceinline__ DmaLane<C> dma_lane(int wave, int lane) {
 // later). Paged sources with power-of-two pages of >= 16 tokens read the
 // tile's page ids with scalar loads, so no vector-memory wait is needed
 // before the addresses are formed.
-template <class C, int D, bool PAGED, bool SCALAR_PAGES>
+template <class C, int D, bool PAGED, bool SCALAR_PAGES, int WHICH>
 __device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLane<C>& L, int wave, int key0,
-                                         int key_end, char* Kst, char* Vst) {
+                                         int key_end, uint32_t Kst, uint32_t Vst) {
   int pg[5] = {0, 0, 0, 0, 0};
   int lp0 = 0;
   if (PAGED && SCALAR_PAGES) {
@@ -647,17 +684,18 @@ __device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLa
       off = key_off<uint16_t, D, true>(src, k);
     }
     const int n = wave * C::PER_WAVE + q;
-    __builtin_amdgcn_global_load_lds((const void*)(src.kb + off + L.colK[q]), GQA_LDS(Kst + n * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(src.vb + off + L.colV[q]), GQA_LDS(Vst + n * 1024), 16, 0, 0);
+    if (WHICH & 1) dma16(src.kb + off + L.colK[q], Kst + n * 1024);
+    if (WHICH & 2) dma16(src.vb + off + L.colV[q], Vst + n * 1024);
   }
 }
 
-template <class C, int D>
+template <class C, int D, int WHICH = 3, typename P>
 __device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const DmaLane<C>& L, int wave, int key0,
-                                             int key_end, char* Kst, char* Vst) {
-  if (!src.paged) dma_tile<C, D, false, false>(src, L, wave, key0, key_end, Kst, Vst);
-  else if (src.shift >= 4) dma_tile<C, D, true, true>(src, L, wave, key0, key_end, Kst, Vst);
-  else dma_tile<C, D, true, false>(src, L, wave, key0, key_end, Kst, Vst);
+                                             int key_end, P* Kp, P* Vp) {
+  const uint32_t Kst = lds_u32(Kp), Vst = lds_u32(Vp);
+  if (!src.paged) dma_tile<C, D, false, false, WHICH>(src, L, wave, key0, key_end, Kst, Vst);
+  else if (src.shift >= 4) dma_tile<C, D, true, true, WHICH>(src, L, wave, key0, key_end, Kst, Vst);
+  else dma_tile<C, D, true, false, WHICH>(src, L, wave, key0, key_end, Kst, Vst);
 }
 
 // Scores of one tile for one wave, then the online softmax with a lazy
@@ -699,23 +737,27 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
     }
   }
   if (MASK) {
+    // Key kl = (compile-time part) + 4h of the tile is visible iff kl <
+    // n_valid and (causal) kpos0 + kl <= row_pos: one compare per score of
+    // the constant part against a per-lane limit.
+    const int lim = min(n_valid, causal ? row_pos - kpos0 + 1 : n_valid) - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < C::SB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool vis = kl < n_valid && (!causal || kpos0 + kl <= row_pos);
-        sacc[kb][r] = vis ? sacc[kb][r] : kNegInf;
-      }
+      for (int r = 0; r < 16; ++r)
+        sacc[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3) < lim) ? sacc[kb][r] : kNegInf;
   }
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < C::SB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  // Lane-local max over its half of the row's keys: the rescale decision
+  // needs no exchange (the ballot spans the wave); only an actual rescale
+  // combines the two halves' maxima, so both keep the same m.
+  mx *= c;
   if (__builtin_amdgcn_ballot_w64(mx > s.m + kTau) != 0) {
-    const float m_new = __builtin_fmaxf(s.m, mx);
+    const float m_new = __builtin_fmaxf(s.m, __builtin_fmaxf(mx, __shfl_xor(mx, 32)));
     const float corr = (m_new == kNegInf) ? 1.f : exp2_fast(s.m - m_new);
     s.l *= corr;
 #pragma unroll
@@ -753,7 +795,7 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
       }
     }
   }
-  s.l += rs + __shfl_xor(rs, 32);
+  s.l += rs;   // sum over this lane's keys; the two halves are added once, at the end
 }
 
 template <class C, int D>
@@ -768,9 +810,6 @@ __device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLa
   else dma_compute<C, D, false>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
 }
 
-__device__ __forceinline__ uint32_t lds_u32(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 // Four ring stages consumed two tiles per barrier: after the barrier of pair
 // p (tiles 2p, 2p+1) the DMA of pair p+1 is issued into the two stages the
@@ -809,8 +848,8 @@ attn_wide_dma(AttnArgs a) {
   if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
 #define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                              \
   {                                                                                                   \
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                                  \
-    __builtin_amdgcn_s_barrier();                                                                     \
+    wait_dma<0>();                                                                                    \
+    lds_barrier();                                                                                    \
     if (j + 2 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);              \
     if (j + 3 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);              \
     dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,  \
@@ -830,6 +869,7 @@ attn_wide_dma(AttnArgs a) {
     }
   }
 #undef GQA_DMA_PAIR
+  s.l += __shfl_xor(s.l, 32);
   write_row<C, uint16_t, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
 }
 
@@ -957,27 +997,28 @@ attn_narrow_dma(AttnArgs a) {
   if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
   if (wave + 4 < nt) dma_tile_any<C, D>(src, L, 0, kb0 + (wave + 4) * C::BN, ke, K1, V1);
   for (int j = wave; j < nt; j += 8) {
-    if (j + 4 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    if (j + 4 < nt) wait_dma<VM>();
+    else wait_dma<0>();
     dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, u, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
                    i, h);
     if (j + 8 < nt) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));   // own LDS reads of stage 0 done
+      wait_dma<63>();   // own LDS reads of stage 0 done
       dma_tile_any<C, D>(src, L, 0, kb0 + (j + 8) * C::BN, ke, K0, V0);
     }
     const int j2 = j + 4;
     if (j2 >= nt) break;
-    if (j2 + 4 < nt) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    if (j2 + 4 < nt) wait_dma<VM>();
+    else wait_dma<0>();
     dma_step<C, D>(lds_u32(K1), lds_u32(V1), L, s, u, kb0 + j2 * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
                    i, h);
     if (j2 + 8 < nt) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+      wait_dma<63>();
       dma_tile_any<C, D>(src, L, 0, kb0 + (j2 + 8) * C::BN, ke, K1, V1);
     }
   }
   // Merge the four waves' states (same rows, disjoint keys) through LDS.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  s.l += __shfl_xor(s.l, 32);
+  wait_dma<0>();
   __syncthreads();
   float* mo = (float*)st0;                       // [wave][db][r][lane]
   float2* mml = (float2*)st1;
