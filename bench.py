@@ -36,7 +36,8 @@ PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 matrix/vector (published)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E (published)
 LLC_BYTES = 256 << 20           # Infinity Cache
 
-WORKLOADS = {"fanout": 3, "decode": 2, "prefill": 4, "mixed": 5, "tiny": 1}
+WORKLOADS = {"fanout": "fanout_8x20_32k", "decode": "decode_8k", "prefill": "prefill_32k",
+             "mixed": "mixed_32dec_64x4", "tiny": "tiny_fp32_fanout"}
 KERNEL_SOURCES = ["gqa_attention_agentic_amd/csrc/attention.hip"]
 
 
@@ -70,14 +71,14 @@ def clone_inputs(inp, n):
     return out
 
 
-def run_workload(k: int, steps: int, warmup: int, log):
-    """Times `steps` forwards of config k; returns a result dict."""
+def run_workload(name: str, steps: int, warmup: int, log):
+    """Times `steps` forwards of the named workload; returns (workload, result dict)."""
     import torch
 
     import gqa_attention_agentic_amd as G
-    from workload import generate, get_config
+    from workload import generate, get_workload
 
-    w = get_config(k)
+    w = get_workload(name)
     t0 = time.time()
     base = generate(w, "cuda")
     kv_bytes = w.kv_bytes()
@@ -167,18 +168,18 @@ def traffic_for(w):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(k: int, budget_s: float, log):
+def cpu_baseline(name: str, budget_s: float, log):
     """The fp64 oracle on this host's cores over whole branches of the same
     workload until about budget_s seconds of CPU work (input generation and
     copies excluded)."""
     import torch
 
     import oracle
-    from workload import generate, get_config
+    from workload import generate, get_workload
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_helpers import cpu_subset
 
-    w = get_config(k)
+    w = get_workload(name)
     torch.set_num_threads(os.cpu_count() or 1)
     inp = generate(w, "cpu")
     done_flops, spent, branches = 0, 0.0, []
@@ -194,7 +195,7 @@ def cpu_baseline(k: int, budget_s: float, log):
             continue
         sub, _ = cpu_subset(inp, [b])
         t0 = time.perf_counter()
-        if k == 4:   # prefill: a bounded row sample across the whole sequence
+        if br.q_len > 1024:   # long prefill: a bounded row sample across the whole sequence
             toks = list(range(0, br.q_len, max(1, br.q_len // 48)))
             oracle.attention(sub, w.num_kv_heads, w.page_size, w.causal, tokens=toks)
             C = w.context_len(br)
@@ -240,13 +241,11 @@ def main():
     import gqa_attention_agentic_amd as G
     G.load()
 
-    k = WORKLOADS[args.workload]
-    w, res = run_workload(k, args.steps, args.warmup, log)
+    w, res = run_workload(WORKLOADS[args.workload], args.steps, args.warmup, log)
     traffic = traffic_for(w)
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
-        ko = WORKLOADS[name]
-        wo, ro = run_workload(ko, max(3, args.steps // 4), 2, log)
+        wo, ro = run_workload(WORKLOADS[name], max(3, args.steps // 4), 2, log)
         ro["roofline"] = roofline_of(wo, ro, traffic_for(wo))
         others[name] = ro
     line = {
@@ -277,7 +276,7 @@ def main():
         "input_copies": res["input_copies"],
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(k, args.cpu_budget, log)
+        line["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget, log)
     line["others"] = others
     print(json.dumps(line), flush=True)
 

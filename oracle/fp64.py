@@ -16,7 +16,7 @@ Sources (page titles; sections as they appear on the pages):
 * same page, §4 -- the (m, l, O) merge: m = max(m_a, m_b), each side scaled
   by exp(m_side - m), the output normalised once at the end.
 
-Readings where the pages leave a step open (listed again in the design doc):
+Readings where the pages leave a step open:
 
 * query head h reads KV head floor(h / G) (contiguous groups);
 * the q_len new tokens of a branch are the last q_len positions of its

@@ -29,9 +29,9 @@ def handle_for(w, **kw):
     return GqaAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype, **kw)
 
 
-def run_library(w, inp, splits="config", handle=None, causal=None):
+def run_library(w, inp, splits="workload", handle=None, causal=None):
     h = handle or handle_for(w)
-    sp = w.splits if splits == "config" else splits
+    sp = w.splits if splits == "workload" else splits
     o, lse = h.forward_inputs(inp, w.causal if causal is None else causal, splits=sp)
     torch.cuda.synchronize()
     return o, lse, h
@@ -114,7 +114,7 @@ def compare(w, o_gpu, lse_gpu, o_ref, lse_ref, tokens, heads=None, label=""):
     return stats
 
 
-def full_parity(w, splits="config", label=None, inp=None):
+def full_parity(w, splits="workload", label=None, inp=None):
     label = label or w.name
     say(f"[parity] {label}: generating")
     inp = inp or generate(w, "cuda")

@@ -19,7 +19,7 @@ import torch.nn.functional as F
 
 import oracle
 from oracle import fp64 as OA
-from workload import custom, generate, get_config
+from workload import custom, generate, get_workload
 from workload.generate import Inputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -119,9 +119,9 @@ def pin_golden_merge():
         assert abs(lse.item() - _parse(g["expected_final"]["lse"])) < 1e-12
 
 
-def pin_brute_force_config1():
+def pin_brute_force_tiny():
     """Pure-Python loops with math.fsum / math.exp on the tiny fp32 fan-out."""
-    w = get_config(1)
+    w = get_workload("tiny_fp32_fanout")
     inp = generate(w, "cpu")
     o, lse = run_oracle(w, inp)
     G = w.group_size
@@ -179,7 +179,7 @@ def _sdpa_check(w, inp):
 def pin_library_sdpa():
     """torch.nn.functional.scaled_dot_product_attention (fp64, CPU) with
     K/V repeated per query head and an explicit boolean mask."""
-    _sdpa_check(get_config(1), generate(get_config(1), "cpu"))
+    _sdpa_check(get_workload("tiny_fp32_fanout"), generate(get_workload("tiny_fp32_fanout"), "cpu"))
     w = custom("sdpa_small", H_q=8, H_kv=2, d=32, page_size=8, shared=(40, 0),
                branches=((0, 3, 21), (0, 6, 9), (1, 1, 30), (1, 4, 4)), seed=7)
     _sdpa_check(w, generate(w, "cpu"))
@@ -414,7 +414,7 @@ def pin_invariant_paging():
 
 ALL_PINS = [
     pin_golden_weights_123, pin_golden_paged_causal, pin_golden_merge,
-    pin_brute_force_config1, pin_library_sdpa, pin_closed_form_zero_q,
+    pin_brute_force_tiny, pin_library_sdpa, pin_closed_form_zero_q,
     pin_closed_form_prefill_row0, pin_closed_form_dominant_key,
     pin_invariant_batching, pin_invariant_split_merge, pin_invariant_causal,
     pin_invariant_gqa_map, pin_invariant_paging,

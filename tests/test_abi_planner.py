@@ -10,7 +10,7 @@ import pytest
 
 import gqa_attention_agentic_amd as G
 from gqa_attention_agentic_amd import _lib
-from workload import custom, get_config
+from workload import custom, get_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -89,7 +89,7 @@ def _covered_pairs(w, items):
 
 
 CASES = [
-    get_config(1),
+    get_workload("tiny_fp32_fanout"),
     custom("fan", H_q=8, H_kv=2, shared=(300,), branches=((0, 5, 37), (0, 7, 50), (0, 20, 100)), seed=1),
     custom("pref", H_q=4, H_kv=1, shared=(700,), branches=((0, 700, 0),), seed=1, splits=[3, 0]),
     custom("mixed", H_q=8, H_kv=2, shared=(0, 130), seed=1,
@@ -119,10 +119,10 @@ def test_split_override_honoured():
             assert used == set(range(sp[slot])), (slot, used)
 
 
-def test_config_split_counts():
-    assert _plan(get_config(1))[1] == [3, 1, 1]
-    assert _plan(get_config(2))[1] == [32, 0]
-    assert _plan(get_config(4))[1] == [8, 0]
+def test_pinned_split_counts():
+    assert _plan(get_workload("tiny_fp32_fanout"))[1] == [3, 1, 1]
+    assert _plan(get_workload("decode_8k"))[1] == [32, 0]
+    assert _plan(get_workload("prefill_32k"))[1] == [8, 0]
 
 
 @pytest.mark.parametrize("dtype,rows", [("bf16", 256), ("fp32", 128)])
@@ -149,10 +149,10 @@ def test_causal_skip_counts_lower_triangle(dtype, rows):
 
 
 def test_heuristic_fills_the_device():
-    items, splits, _ = _plan(get_config(3))
+    items, splits, _ = _plan(get_workload("fanout_8x20_32k"))
     wide = [it for it in items if it[7] == 0]
     assert 256 <= len(wide) <= 1024, len(wide)
-    items, splits, _ = _plan(get_config(5))
+    items, splits, _ = _plan(get_workload("mixed_32dec_64x4"))
     assert all(s >= 1 for s in splits[1:])
 
 

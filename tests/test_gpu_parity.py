@@ -12,7 +12,7 @@ import random
 import pytest
 import torch
 
-from workload import custom, generate, get_config
+from workload import custom, generate, get_workload
 from workload.generate import Inputs
 
 import gpu_helpers as H
@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 SMALL = {
-    "tiny_fp32_fanout": lambda: get_config(1),
+    "tiny_fp32_fanout": lambda: get_workload("tiny_fp32_fanout"),
     "fanout_bf16_d128": lambda: custom("fanout_bf16_d128", H_q=16, H_kv=2, d=128, page_size=16,
                                        shared=(1000,), branches=((0, 5, 37), (0, 7, 50), (0, 20, 100)),
                                        seed=101),
@@ -158,44 +158,44 @@ def test_causal_future_keys_ignored():
 
 
 # ------------------------------------------------ full-size configurations --
-def _sample_parity(k, branches, tokens):
-    w = get_config(k)
-    H.say(f"[parity] config {k} ({w.name}): generating")
+def _sample_parity(name, branches, tokens):
+    w = get_workload(name)
+    H.say(f"[parity] {name}: generating")
     inp = generate(w, "cuda")
-    H.say(f"[parity] config {k}: library")
+    H.say(f"[parity] {name}: library")
     o, lse, h = H.run_library(w, inp)
-    H.say(f"[parity] config {k}: plan {h.plan_stats()} splits {h.plan_splits()[:6]}")
-    H.say(f"[parity] config {k}: oracle on {len(tokens)} tokens")
+    H.say(f"[parity] {name}: plan {h.plan_stats()} splits {h.plan_splits()[:6]}")
+    H.say(f"[parity] {name}: oracle on {len(tokens)} tokens")
     o_ref, l_ref, toks = H.oracle_rows(w, inp, branches=branches, tokens=tokens)
-    return H.compare(w, o, lse, o_ref, l_ref, toks, label=f"config {k}")
+    return H.compare(w, o, lse, o_ref, l_ref, toks, label=name)
 
 
-def test_config1_full():
-    H.full_parity(get_config(1))
+def test_tiny_fp32_fanout_full():
+    H.full_parity(get_workload("tiny_fp32_fanout"))
 
 
-def test_config2_full():
-    _sample_parity(2, [0], [0])
+def test_decode_8k_full():
+    _sample_parity("decode_8k", [0], [0])
 
 
-def test_config3_sampled():
+def test_fanout_8x20_32k_sampled():
     rng = random.Random(3)
     toks = sorted({b * 20 + t for b in range(8) for t in (0, 19, rng.randrange(20))})
-    _sample_parity(3, list(range(8)), toks)
+    _sample_parity("fanout_8x20_32k", list(range(8)), toks)
 
 
 @pytest.mark.timeout(600)
-def test_config4_sampled():
+def test_prefill_32k_sampled():
     rng = random.Random(4)
     # shard boundaries (4096 multiples), KV tile edges, M-tile edges, the last rows
     toks = {0, 1, 15, 16, 63, 64, 4095, 4096, 4097, 8191, 12288, 20479, 28672, 32767}
     toks |= {rng.randrange(32768) for _ in range(4)}
-    _sample_parity(4, [0], sorted(toks))
+    _sample_parity("prefill_32k", [0], sorted(toks))
 
 
 @pytest.mark.timeout(600)
-def test_config5_sampled():
-    w = get_config(5)
+def test_mixed_32dec_64x4_sampled():
+    w = get_workload("mixed_32dec_64x4")
     rng = random.Random(5)
     lens = [b.private_len for b in w.branches[:32]]
     dec = sorted({lens.index(max(lens)), lens.index(min(lens))} | set(rng.sample(range(32), 4)))
@@ -204,4 +204,4 @@ def test_config5_sampled():
     for b in w.branches:
         qb.append(qb[-1] + b.q_len)
     toks = [qb[b] for b in dec] + [qb[b] + t for b in fan for t in (0, 3)]
-    _sample_parity(5, dec + fan, toks)
+    _sample_parity("mixed_32dec_64x4", dec + fan, toks)

@@ -6,5 +6,5 @@ the HIP path (``gqa_attention_agentic_amd``) can take their inputs from it
 without sharing any code of the method.
 """
 
-from .configs import Workload, CONFIGS, get_config, custom, Branch, Group  # noqa: F401
+from .configs import Workload, WORKLOADS, get_workload, custom, Branch, Group  # noqa: F401
 from .generate import generate, Inputs  # noqa: F401

@@ -135,7 +135,7 @@ def _llama(name, groups, branches, causal, seed, splits=None, dtype="bf16",
                     description=description, random_private=random_private)
 
 
-def config1() -> Workload:
+def tiny_fp32_fanout() -> Workload:
     """Tiny fp32 fan-out: 1 KV head, G=2, d=64, 2 branches x 4 new tokens,
     shared prefix 64, private suffix 8 per branch in pages of 4, 4 shards
     per row (3 over the prefix + the suffix)."""
@@ -147,7 +147,7 @@ def config1() -> Workload:
         description="tiny fp32 fan-out, 2 branches x 4 queries, prefix 64, suffix 8, pages of 4")
 
 
-def config2() -> Workload:
+def decode_8k() -> Workload:
     """Llama3-70B single-layer decode: batch 1, T_q = 1, 8192 contiguous
     keys, 32 shards, attends the whole past."""
     return _llama("decode_8k", [Group(8192)], [Branch(0, 1, 0)], causal=False,
@@ -155,7 +155,7 @@ def config2() -> Workload:
                   description="Llama3-70B decode, 1 token over 8192 contiguous keys, 32 shards")
 
 
-def config3() -> Workload:
+def fanout_8x20_32k() -> Workload:
     """Agentic fan-out: 8 sub-agents x 20 new tokens over a 32768-token
     shared prefix, 512 private tokens per branch in 16-token pages."""
     return _llama("fanout_8x20_32k", [Group(32768)],
@@ -163,14 +163,14 @@ def config3() -> Workload:
                   description="8 sub-agents x 20 tokens, shared prefix 32768, 512 private tokens each")
 
 
-def config4() -> Workload:
+def prefill_32k() -> Workload:
     """Long-context causal prefill of 32768 tokens, 8 KV shards."""
     return _llama("prefill_32k", [Group(32768)], [Branch(0, 32768, 0)],
                   causal=True, seed=4, splits=[8, 0],
                   description="causal prefill of 32768 tokens, 8 shards")
 
 
-def config5() -> Workload:
+def mixed_32dec_64x4() -> Workload:
     """Mixed: 32 independent decodes with KV lengths drawn from
     U{1024..65536}, plus a 64 x 4 fan-out over a 65536-token prefix with
     128 private tokens per branch."""
@@ -184,11 +184,12 @@ def config5() -> Workload:
                   description="32 decodes with lengths U{1024..65536} + 64 x 4 fan-out over 65536 prefix")
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {f.__name__: f for f in (tiny_fp32_fanout, decode_8k, fanout_8x20_32k, prefill_32k,
+                                      mixed_32dec_64x4)}
 
 
-def get_config(k: int) -> Workload:
-    return CONFIGS[k]()
+def get_workload(name: str) -> Workload:
+    return WORKLOADS[name]()
 
 
 def custom(name: str, *, dtype="bf16", H_q=16, H_kv=2, d=128, page_size=16,

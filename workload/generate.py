@@ -4,7 +4,7 @@ Recipe (one torch.Generator seeded with the workload's seed, on the device
 the tensors are made on):
 
 1. for workloads with random private lengths, the lengths are drawn first
-   (``configs.config5`` makes the same draw);
+   (``configs.mixed_32dec_64x4`` makes the same draw);
 2. Q, shared K, shared V, private K pages, private V pages are drawn from
    N(0, 1) in fp32, in that order and in fixed 16M-element chunks, then
    rounded to the storage dtype with round-to-nearest-even;
