@@ -225,6 +225,9 @@ def main():
                     help="comma list of secondary workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB each, so that byte counters read "
+                         "under a profiler can be scaled by a copy of known size")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -240,6 +243,15 @@ def main():
         sys.exit(1)
     import gqa_attention_agentic_amd as G
     G.load()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration: 3 device copies of {n} bytes")
+        del src, dst
 
     w, res = run_workload(WORKLOADS[args.workload], args.steps, args.warmup, log)
     traffic = traffic_for(w)

@@ -34,9 +34,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Kernel-only timing of one forward: each launch records its own pair of
+// events around the kernel's execution.
 struct TimerSlot {
-  hipEvent_t ev[4];   // attention start, attention end, merge start, merge end
-  bool merged;
+  hipEvent_t ev[6];   // wide start/end, narrow start/end, merge start/end
+  bool wide, narrow, merged;
 };
 
 }  // namespace
@@ -355,24 +357,25 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   a.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
 
   TimerSlot* tm = h->timing ? next_timer(h) : nullptr;
-  if (tm) hipEventRecord(tm->ev[0], st);
+  auto ev = [&](int k) -> hipEvent_t { return tm ? tm->ev[k] : nullptr; };
+  if (tm) {
+    tm->wide = !Q.wide.empty();
+    tm->narrow = !Q.narrow.empty();
+    tm->merged = Q.merge_rows > 0;
+  }
   if (!Q.wide.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
-    e = gqa::launch_attention(a, (int32_t)Q.wide.size(), false, h->p.dtype, h->p.head_dim, st);
+    e = gqa::launch_attention(a, (int32_t)Q.wide.size(), false, h->p.dtype, h->p.head_dim, st, ev(0), ev(1));
     if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
   }
   if (!Q.narrow.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
-    e = gqa::launch_attention(a, (int32_t)Q.narrow.size(), true, h->p.dtype, h->p.head_dim, st);
+    e = gqa::launch_attention(a, (int32_t)Q.narrow.size(), true, h->p.dtype, h->p.head_dim, st, ev(2), ev(3));
     if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
   }
-  if (tm) hipEventRecord(tm->ev[1], st);
-  if (tm) tm->merged = Q.merge_rows > 0;
   if (Q.merge_rows > 0) {
-    if (tm) hipEventRecord(tm->ev[2], st);
-    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, Q.max_row_parts, st);
+    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, Q.max_row_parts, st, ev(4), ev(5));
     if (e != hipSuccess) return hip_fail(e, "merge launch");
-    if (tm) hipEventRecord(tm->ev[3], st);
   }
   return GQA_OK;
 }
@@ -405,16 +408,15 @@ gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
   double at = 0.0, mg = 0.0;
   for (size_t k = 0; k < h->timers_used; ++k) {
     TimerSlot& t = h->timers[k];
-    hipError_t e = hipEventSynchronize(t.merged ? t.ev[3] : t.ev[1]);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    float ms = 0.f;
-    e = hipEventElapsedTime(&ms, t.ev[0], t.ev[1]);
-    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-    at += ms;
-    if (t.merged) {
-      e = hipEventElapsedTime(&ms, t.ev[2], t.ev[3]);
+    const bool used[3] = {t.wide, t.narrow, t.merged};
+    for (int j = 0; j < 3; ++j) {
+      if (!used[j]) continue;
+      hipError_t e = hipEventSynchronize(t.ev[2 * j + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, t.ev[2 * j], t.ev[2 * j + 1]);
       if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-      mg += ms;
+      (j < 2 ? at : mg) += ms;
     }
   }
   *attn_ms = at;

@@ -36,6 +36,7 @@
 //  * A row with exactly one live partial in total writes O / l and LSE
 //    directly (ADR-0060, §0.5.4 N = 1); otherwise the unnormalised partial
 //    (m, l, O) goes to the workspace for the merge kernel (§4).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1130,16 +1131,21 @@ lse_merge(AttnArgs a) {
   }
 }
 
+#define GQA_LAUNCH(KERNEL, GRID, BLOCK) \
+  hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), 0, st, e0, e1, 0, a)
+
 template <typename T, int D>
-hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStream_t st) {
+hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStream_t st, hipEvent_t e0,
+                         hipEvent_t e1) {
   if (n_items <= 0) return hipSuccess;
   if (narrow) {
-    if constexpr (std::is_same<T, uint16_t>::value)
-      hipLaunchKernelGGL((attn_narrow_dma<D>), dim3(n_items), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_narrow<T, D>), dim3(n_items), dim3(256), 0, st, a);
-  } else if constexpr (std::is_same<T, uint16_t>::value)
-    hipLaunchKernelGGL((attn_wide_dma<D>), dim3(n_items), dim3(512), 0, st, a);
-  else hipLaunchKernelGGL((attn_wide<T, D>), dim3(n_items), dim3(256), 0, st, a);
+    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_items, 256);
+    else GQA_LAUNCH((attn_narrow<T, D>), n_items, 256);
+  } else if constexpr (std::is_same<T, uint16_t>::value) {
+    GQA_LAUNCH((attn_wide_dma<D>), n_items, 512);
+  } else {
+    GQA_LAUNCH((attn_wide<T, D>), n_items, 256);
+  }
   return hipGetLastError();
 }
 
@@ -1147,34 +1153,36 @@ hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStr
 // the largest row needs (up to 16), fewer when rows have few partials so the
 // kernel keeps its occupancy.
 template <typename T, int D>
-hipError_t launch_merge_t(const AttnArgs& a, int max_parts, hipStream_t st) {
+hipError_t launch_merge_t(const AttnArgs& a, int max_parts, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   const int64_t blocks = (int64_t)a.n_q_tokens * a.H_kv;
   if (blocks <= 0) return hipSuccess;
-  if (max_parts <= 4) hipLaunchKernelGGL((lse_merge<T, D, 4>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else if (max_parts <= 8) hipLaunchKernelGGL((lse_merge<T, D, 8>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((lse_merge<T, D, 16>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (max_parts <= 4) GQA_LAUNCH((lse_merge<T, D, 4>), (unsigned)blocks, 256);
+  else if (max_parts <= 8) GQA_LAUNCH((lse_merge<T, D, 8>), (unsigned)blocks, 256);
+  else GQA_LAUNCH((lse_merge<T, D, 16>), (unsigned)blocks, 256);
   return hipGetLastError();
 }
+#undef GQA_LAUNCH
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int dtype, int head_dim,
-                            hipStream_t stream) {
+                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (dtype == 0) {
-    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, n_items, narrow, stream);
-    return launch_attn_t<uint16_t, 64>(a, n_items, narrow, stream);
+    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, n_items, narrow, stream, ev_start, ev_stop);
+    return launch_attn_t<uint16_t, 64>(a, n_items, narrow, stream, ev_start, ev_stop);
   }
-  if (head_dim == 128) return launch_attn_t<float, 128>(a, n_items, narrow, stream);
-  return launch_attn_t<float, 64>(a, n_items, narrow, stream);
+  if (head_dim == 128) return launch_attn_t<float, 128>(a, n_items, narrow, stream, ev_start, ev_stop);
+  return launch_attn_t<float, 64>(a, n_items, narrow, stream, ev_start, ev_stop);
 }
 
-hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream) {
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream,
+                        hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (dtype == 0) {
-    if (head_dim == 128) return launch_merge_t<uint16_t, 128>(a, max_parts, stream);
-    return launch_merge_t<uint16_t, 64>(a, max_parts, stream);
+    if (head_dim == 128) return launch_merge_t<uint16_t, 128>(a, max_parts, stream, ev_start, ev_stop);
+    return launch_merge_t<uint16_t, 64>(a, max_parts, stream, ev_start, ev_stop);
   }
-  if (head_dim == 128) return launch_merge_t<float, 128>(a, max_parts, stream);
-  return launch_merge_t<float, 64>(a, max_parts, stream);
+  if (head_dim == 128) return launch_merge_t<float, 128>(a, max_parts, stream, ev_start, ev_stop);
+  return launch_merge_t<float, 64>(a, max_parts, stream, ev_start, ev_stop);
 }
 
 }  // namespace gqa

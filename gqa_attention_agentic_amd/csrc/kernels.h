@@ -37,11 +37,15 @@ struct AttnArgs {
 };
 
 // Attention over a work-item list. narrow selects the 32-row kernel.
+// ev_start / ev_stop (may be null) are recorded by the launch itself around
+// the kernel's execution (hipExtLaunchKernelGGL), for kernel-only timing.
 hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int dtype,
-                            int head_dim, hipStream_t stream);
+                            int head_dim, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                            hipEvent_t ev_stop = nullptr);
 
 // Log-sum-exp merge of the partials of every output row with >= 2 of them.
 // max_parts: the largest number of partials any output row has.
-hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream,
+                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 }  // namespace gqa

@@ -148,11 +148,13 @@ gqa_status gqa_attn_plan_stats(const gqa_attn* h, gqa_plan_stats* out);
  * unit without keys or without queries). */
 gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n);
 
-/* Kernel timing with HIP events recorded on the forward's stream around each
- * kernel. enable != 0 starts recording (and clears earlier records).
+/* Kernel timing with HIP events that each launch records around its own
+ * kernel's execution on the forward's stream (hipExtLaunchKernelGGL start /
+ * stop events). enable != 0 starts recording (and clears earlier records).
  * gqa_attn_kernel_times waits for the recorded events and returns the summed
- * milliseconds of every forward since timing was enabled and the number of
- * forwards, then clears the records. */
+ * milliseconds of every forward since timing was enabled -- attn_ms sums the
+ * attention launches (wide and narrow), merge_ms the merge launch -- and the
+ * number of forwards, then clears the records. */
 gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable);
 gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
                                  int64_t* n_forwards);
