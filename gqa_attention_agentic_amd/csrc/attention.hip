@@ -550,15 +550,13 @@ attn_wide(AttnArgs a) {
 
 // ------------------------------------------------------ wide, bf16, DMA ----
 // The MFMA-bound kernel for bf16: 8 waves (256 rows, 32 per wave, 2 waves
-// per SIMD) share a 3-stage ring of 64-key K/V tiles in LDS that global->LDS
+// per SIMD) share a 4-stage ring of 64-key K/V tiles in LDS that global->LDS
 // DMA (global_load_lds_dwordx4) fills two tiles ahead of the compute, with
 // no register staging. LDS rows are unpadded and XOR-swizzled per 16-byte
-// chunk so that both operand reads are bank-conflict free: K by the key's
-// low 3 bits (ds_read_b128 of 8 consecutive keys hits 8 distinct chunks), V
-// by 2x the key's low 2 bits (the 16-lane groups of ds_read_b64_tr_b16 read
-// 4 keys x 32 bytes, landing in 4 distinct 32-byte bank segments). The
-// transposing LDS read turns V's [key][d] rows into the k-contiguous operand
-// of O^T += V^T P^T without any transpose on the store side.
+// chunk (swz_k / swz_v below) so that both operand reads are free of bank
+// conflicts. The transposing LDS read turns V's [key][d] rows into the
+// k-contiguous operand of O^T += V^T P^T without any transpose on the store
+// side.
 template <int D>
 struct DmaCfg {
   static constexpr bool BF16 = true;
@@ -618,14 +616,35 @@ __device__ __forceinline__ uint32_t lds_u32(const char* p) {
 }
 __device__ __forceinline__ uint32_t lds_u32(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
+// LDS swizzle of a K or V tile row (one key, ROW bytes = ROW/16 chunks of 16
+// bytes): logical chunk c of key k sits at physical chunk c ^ swz(k). The
+// LDS serves 16 lanes of a 16-byte read (or 32 lanes of an 8-byte read) per
+// cycle across 64 four-byte banks, i.e. 16 chunk slots, and a key row of
+// d = 128 (256 bytes) covers all 16 slots, so:
+//  * K operand (ds_read_b128): the 16 lanes of a cycle read one logical
+//    chunk of 16 consecutive keys; XOR with key & 15 spreads them over all
+//    16 slots (d = 64: rows alternate slot halves, XOR with bits 1..3).
+//  * V operand (ds_read_b64_tr_b16): the 32 lanes of a cycle read 4
+//    consecutive keys x 4 logical chunks; XOR with 4 (key & 3) moves each
+//    key to its own group of 4 slots (d = 64: 4 ((key >> 1) & 1)).
+template <int ROW>
+__device__ __forceinline__ int swz_k(int key) {
+  static_assert(ROW == 256 || ROW == 128, "swizzles are laid out for d = 128 and d = 64");
+  return ROW == 256 ? (key & 15) : ((key >> 1) & 7);
+}
+template <int ROW>
+__device__ __forceinline__ int swz_v(int key) {
+  return ROW == 256 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+}
+
 template <class C>
 struct DmaLane {
   // per-lane constants of the DMA (global side) and of the operand reads (LDS side)
   int key_rel[C::PER_WAVE];   // tile-relative key of this lane's chunk in instruction q
   int colK[C::PER_WAVE];      // element offset inside the key row (logical chunk * 8)
   int colV[C::PER_WAVE];
-  int kaddr[4];                       // byte offset of K operand chunk for ks = 0..3 (ks+4: +128)
-  int vaddr[2];                       // byte offset of the V tr16 read for db = 0, 1 (db+2: +128)
+  int kaddr[C::QF];           // byte offset of the K operand chunk for ks (key block kb adds kb * 32 rows)
+  int vaddr[C::OB];           // byte offset of the V tr16 read for db (16-key chunk kc adds 16 kc rows)
 };
 
 template <class C>
@@ -637,17 +656,21 @@ __device__ __forceinline__ DmaLane<C> dma_lane(int wave, int lane) {
     const int kr = byte / C::ROW;
     const int pc = (byte % C::ROW) / 16;
     L.key_rel[q] = kr;
-    L.colK[q] = (pc ^ (kr & 7)) * 8;
-    L.colV[q] = (pc ^ (2 * (kr & 3))) * 8;
+    L.colK[q] = (pc ^ swz_k<C::ROW>(kr)) * 8;
+    L.colV[q] = (pc ^ swz_v<C::ROW>(kr)) * 8;
   }
   const int i = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) L.kaddr[ks] = i * C::ROW + 16 * ((2 * ks + h) ^ (i & 7));
+  for (int ks = 0; ks < C::QF; ++ks) L.kaddr[ks] = i * C::ROW + 16 * ((2 * ks + h) ^ swz_k<C::ROW>(i));
+  // V^T fragment through ds_read_b64_tr_b16: in 16-lane group g, lane j
+  // supplies 4 elements of key 4 (g >> 1) + (j >> 2), d = 32 db + 16 (g & 1)
+  // + 4 (j & 3); the transpose hands lane j of the group d = ... + j for 4
+  // consecutive keys.
   const int g = lane >> 4, j = lane & 15, half = g & 1, hh = g >> 1;
+  const int key0 = 4 * hh + (j >> 2);
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
-    L.vaddr[db] = (4 * hh + (j >> 2)) * C::ROW + 16 * ((4 * db + 2 * half + ((j >> 1) & 1)) ^ (2 * (j >> 2))) +
-                  8 * (j & 1);
+  for (int db = 0; db < C::OB; ++db)
+    L.vaddr[db] = key0 * C::ROW + 16 * ((4 * db + 2 * half + ((j >> 1) & 1)) ^ swz_v<C::ROW>(key0)) + 8 * (j & 1);
   return L;
 }
 
@@ -715,16 +738,16 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
   typedef __attribute__((address_space(3))) const bf16x8_t* lds_bf16x8;
   typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16;
   // Per-call opaque bases: every operand address below is base + immediate.
-  uint32_t kb4[4], vb2[2];
+  uint32_t kbs[C::QF], vbs[C::OB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    kb4[q] = kst + L.kaddr[q];
-    asm volatile("" : "+v"(kb4[q]));
+  for (int q = 0; q < C::QF; ++q) {
+    kbs[q] = kst + L.kaddr[q];
+    asm volatile("" : "+v"(kbs[q]));
   }
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    vb2[q] = vst + L.vaddr[q];
-    asm volatile("" : "+v"(vb2[q]));
+  for (int q = 0; q < C::OB; ++q) {
+    vbs[q] = vst + L.vaddr[q];
+    asm volatile("" : "+v"(vbs[q]));
   }
   f32x16_t sacc[C::SB];
 #pragma unroll
@@ -733,7 +756,7 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
     for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8_t av = *(lds_bf16x8)(uintptr_t)(kb4[ks & 3] + kb * 32 * C::ROW + (ks >> 2) * 128);
+      const bf16x8_t av = *(lds_bf16x8)(uintptr_t)(kbs[ks] + kb * 32 * C::ROW);
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s.qf[ks], sacc[kb], 0, 0, 0);
     }
   }
@@ -788,7 +811,7 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
       const int krow = (16 * (2 * kb + cc)) * C::ROW;
 #pragma unroll
       for (int db = 0; db < C::OB; ++db) {
-        const uint32_t va = vb2[db & 1] + krow + (db >> 1) * 128;
+        const uint32_t va = vbs[db] + krow;
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)va);
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)(va + 8 * C::ROW));
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
