@@ -56,6 +56,8 @@ class GqaAttention:
         _lib.check(self.lib.gqa_attn_create(ctypes.byref(p), ctypes.byref(h)))
         self._h = h
         self._n_units = 0
+        self._meta_key = None
+        self._meta_arrays = None
 
     # ------------------------------------------------------------ forward --
     def forward(self, q, k_shared, v_shared, k_pages, v_pages, page_table,
@@ -64,31 +66,36 @@ class GqaAttention:
                 branch_private_len: Sequence[int], causal: bool,
                 splits: Optional[Sequence[int]] = None, out=None, lse=None, stream=None):
         import torch
-        dev = q.device
         want = torch.bfloat16 if self.dtype_code == _lib.GQA_BF16 else torch.float32
+        dev = q.get_device()
         for name, t in (("q", q), ("k_shared", k_shared), ("v_shared", v_shared),
                         ("k_pages", k_pages), ("v_pages", v_pages)):
-            if t.dtype != want or t.device != dev or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous {want} tensor on {dev}")
-        if page_table.dtype != torch.int32 or page_table.device != dev or not page_table.is_contiguous():
+            if t.dtype != want or t.get_device() != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor on {q.device}")
+        if page_table.dtype != torch.int32 or page_table.get_device() != dev or not page_table.is_contiguous():
             raise ValueError("page_table must be a contiguous int32 tensor on the same device")
         n_tok = q.shape[0]
         if out is None:
             out = torch.empty_like(q)
         if lse is None:
-            lse = torch.empty(n_tok, self.num_q_heads, dtype=torch.float32, device=dev)
+            lse = torch.empty(n_tok, self.num_q_heads, dtype=torch.float32, device=q.device)
         if stream is None:
-            stream = torch.cuda.current_stream(dev).cuda_stream
-        ng, nb = len(group_shared_start), len(branch_group)
-        _check_lengths(ng, nb, group_shared_len, branch_q_len, branch_private_len, splits)
-        ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() > 0 else 0)
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        # Metadata arrays are converted once per distinct metadata (compared by value).
+        meta = (tuple(group_shared_start), tuple(group_shared_len), tuple(branch_group), tuple(branch_q_len),
+                tuple(branch_private_len), None if splits is None else tuple(splits))
+        if meta != self._meta_key:
+            ng, nb = len(meta[0]), len(meta[2])
+            _check_lengths(ng, nb, meta[1], meta[3], meta[4], meta[5])
+            self._meta_arrays = tuple(_lib.int_array(x) for x in meta)
+            self._meta_key = meta
+        gs, gl, bg, bq, bp, sp = self._meta_arrays
+        ng, nb = len(meta[0]), len(meta[2])
+        ptr = lambda t: t.data_ptr() if t.numel() > 0 else None
         st = self.lib.gqa_attn_forward(
-            self._h, ptr(q), ptr(k_shared), ptr(v_shared), int(k_shared.shape[1]), ptr(k_pages), ptr(v_pages), ptr(page_table),
-            int(page_table.shape[1]) if page_table.dim() == 2 else 0,
-            ng, _lib.int_array(group_shared_start), _lib.int_array(group_shared_len),
-            nb, _lib.int_array(branch_group), _lib.int_array(branch_q_len),
-            _lib.int_array(branch_private_len), _lib.int_array(splits), int(bool(causal)),
-            ptr(out), ptr(lse), ctypes.c_void_p(stream))
+            self._h, ptr(q), ptr(k_shared), ptr(v_shared), k_shared.shape[1], ptr(k_pages), ptr(v_pages),
+            ptr(page_table), page_table.shape[1] if page_table.dim() == 2 else 0,
+            ng, gs, gl, nb, bg, bq, bp, sp, int(bool(causal)), ptr(out), ptr(lse), stream)
         _lib.check(st)
         self._n_units = ng + nb
         return out, lse

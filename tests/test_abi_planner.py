@@ -15,11 +15,11 @@ from workload import custom, get_workload
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _plan(w, splits="config"):
+def _plan(w, splits="workload"):
     return G.plan_host(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, w.group_shared_start(),
                        [g.shared_len for g in w.groups], [b.group for b in w.branches],
                        [b.q_len for b in w.branches], [b.private_len for b in w.branches], w.causal,
-                       splits=w.splits if splits == "config" else splits, dtype=w.dtype)
+                       splits=w.splits if splits == "workload" else splits, dtype=w.dtype)
 
 
 def test_library_exports_every_declared_symbol():
@@ -188,3 +188,49 @@ def test_bad_split_list_rejected():
     with pytest.raises(ValueError) as e:
         G.plan_host(8, 2, 128, 16, [0], [10], [0], [1], [0], True, splits=[1])
     assert "splits_override" in str(e.value)
+
+
+class _StubLib:
+    """Records the metadata arrays the binding hands to gqa_attn_forward."""
+
+    def __init__(self):
+        self.calls = []
+
+    def gqa_attn_forward(self, *args):
+        self.calls.append(args)
+        return 0
+
+
+def _stub_handle():
+    h = object.__new__(G.GqaAttention)
+    h.lib, h._h, h.dtype_code, h.num_q_heads = _StubLib(), None, _lib.GQA_BF16, 4
+    h._meta_key = h._meta_arrays = None
+    h._n_units = 0
+    return h
+
+
+def test_binding_reuses_metadata_arrays_and_sees_changes():
+    """The binding converts the host metadata once per distinct value: a
+    repeated call reuses the arrays, an in-place change of a list is seen,
+    and wrong lengths are rejected before the library is called."""
+    import torch
+    h = _stub_handle()
+    q = torch.zeros(3, 4, 8, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 16, 8, dtype=torch.bfloat16)
+    pages = torch.zeros(2, 1, 4, 8, dtype=torch.bfloat16)
+    table = torch.zeros(1, 2, dtype=torch.int32)
+    gl, bq, bp = [16], [3], [5]
+    args = (q, kv, kv, pages, pages, table, [0], gl, [0], bq, bp, True)
+    h.forward(*args, stream=0)
+    h.forward(*args, stream=0)
+    a, b = h.lib.calls
+    assert all(x is y for x, y in zip(a[10:16], b[10:16]))   # same ctypes arrays reused
+    bp[0] = 6                                                # caller edits a list in place
+    h.forward(*args, stream=0)
+    c = h.lib.calls[-1]
+    assert list(c[15])[:1] == [6]
+    with pytest.raises(ValueError):
+        h.forward(q, kv, kv, pages, pages, table, [0], gl, [0], bq, [5, 5], True, stream=0)
+    with pytest.raises(ValueError):
+        h.forward(q.float(), kv, kv, pages, pages, table, [0], gl, [0], bq, bp, True, stream=0)
+    assert len(h.lib.calls) == 3
