@@ -855,6 +855,13 @@ attn_wide_dma(AttnArgs a) {
   const WorkItem it = a.items[blockIdx.x];
   const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
+  const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+  const DmaLane<C> L = dma_lane<C>(wave, lane);
+  const int kb0 = it.key_begin, ke = it.key_end;
+  const int nt = (ke - kb0 + C::BN - 1) / C::BN;
+  // The first pair's DMA goes out before the row bookkeeping and Q loads.
+  dma_tile_any<C, D>(src, L, wave, kb0, ke, k0, v0);
+  if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
   const int rloc = wave * 32 + i;
   const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
   State<C> s;
@@ -862,14 +869,7 @@ attn_wide_dma(AttnArgs a) {
   int pmin, pmax;
   wave_pos_range(w, &pmin, &pmax);
   const bool active = wave * 32 < it.n_rows;
-  const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
-  const DmaLane<C> L = dma_lane<C>(wave, lane);
   const float c = a.scale_log2;
-  const int kb0 = it.key_begin, ke = it.key_end;
-  const int nt = (ke - kb0 + C::BN - 1) / C::BN;
-
-  dma_tile_any<C, D>(src, L, wave, kb0, ke, k0, v0);
-  if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
 #define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                              \
   {                                                                                                   \
     wait_dma<0>();                                                                                    \
@@ -1002,15 +1002,8 @@ attn_narrow_dma(AttnArgs a) {
   const WorkItem it = a.items[blockIdx.x];
   const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
-  const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
-  State<C> s;
-  load_q<C, uint16_t, D>(a, w, it.kv, h, s);
-  int pmin, pmax;
-  wave_pos_range(w, &pmin, &pmax);
-  const bool active = it.n_rows > 0;
   const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
   const DmaLane<C> L = dma_lane<C>(0, lane);
-  const float c = a.scale_log2;
   const int kb0 = it.key_begin, ke = it.key_end, causal = a.causal;
   const int nt = (ke - kb0 + C::BN - 1) / C::BN;
   constexpr int VM = 2 * C::NINST;
@@ -1018,8 +1011,17 @@ attn_narrow_dma(AttnArgs a) {
   char* V0 = K0 + C::TB;
   char* K1 = st1 + wave * 2 * C::TB;
   char* V1 = K1 + C::TB;
+  // The first tiles' DMA goes out before the row bookkeeping and Q loads,
+  // whose dependent lookups would otherwise delay it.
   if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
   if (wave + 4 < nt) dma_tile_any<C, D>(src, L, 0, kb0 + (wave + 4) * C::BN, ke, K1, V1);
+  const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+  State<C> s;
+  load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+  int pmin, pmax;
+  wave_pos_range(w, &pmin, &pmax);
+  const bool active = it.n_rows > 0;
+  const float c = a.scale_log2;
   for (int j = wave; j < nt; j += 8) {
     if (j + 4 < nt) wait_dma<VM>();
     else wait_dma<0>();
