@@ -47,6 +47,7 @@ struct gqa_attn {
   gqa_attn_params p{};
   int device = 0;
   int n_cu = 256;
+  int wide_per_cu = 1, narrow_per_cu = 1;   // resident workgroups per CU of each attention kernel
   // plan cache
   std::vector<int32_t> key;
   gqa::Plan plan;
@@ -57,7 +58,8 @@ struct gqa_attn {
   char* h_staging = nullptr;
   size_t h_staging_cap = 0;
   hipEvent_t staging_free = nullptr;   // recorded after the last staging -> device copy
-  size_t off_wide = 0, off_narrow = 0, off_units = 0, off_branches = 0, off_tiles = 0;
+  size_t off_wide = 0, off_narrow = 0, off_wide_bins = 0, off_narrow_bins = 0, off_units = 0, off_branches = 0,
+         off_tiles = 0;
   // partial workspace
   char* d_work = nullptr;
   size_t d_work_cap = 0;
@@ -87,7 +89,8 @@ gqa_status check_params(const gqa_attn_params* p) {
 
 gqa_status make_input(const gqa_attn_params* p, int32_t n_groups, const int32_t* gs, const int32_t* gl,
                       int32_t n_branches, const int32_t* bg, const int32_t* bq, const int32_t* bp,
-                      const int32_t* splits, int32_t causal, int n_cu, gqa::PlanInput* in) {
+                      const int32_t* splits, int32_t causal, int n_cu, int wide_per_cu, int narrow_per_cu,
+                      gqa::PlanInput* in) {
   if (n_groups < 0 || n_branches < 0) return fail(GQA_ERR_INVALID_ARG, "negative group or branch count");
   if (n_groups > 0 && (!gs || !gl)) return fail(GQA_ERR_INVALID_ARG, "group arrays are NULL");
   if (n_branches > 0 && (!bg || !bq || !bp)) return fail(GQA_ERR_INVALID_ARG, "branch arrays are NULL");
@@ -99,6 +102,8 @@ gqa_status make_input(const gqa_attn_params* p, int32_t n_groups, const int32_t*
   in->dtype = p->dtype;
   in->causal = causal;
   in->n_cu = n_cu;
+  in->wide_per_cu = wide_per_cu;
+  in->narrow_per_cu = narrow_per_cu;
   in->g_start.assign(gs, gs + n_groups);
   in->g_len.assign(gl, gl + n_groups);
   in->b_group.assign(bg, bg + n_branches);
@@ -121,7 +126,8 @@ void fill_stats(const gqa::Plan& P, int64_t D, gqa_plan_stats* s) {
   s->reserved = 0;
 }
 
-// Serialised plan: wide items | narrow items | units | branches | tiles.
+// Serialised plan: wide items | narrow items | wide bins | narrow bins |
+// units | branches | tiles.
 size_t plan_layout(gqa_attn* h) {
   const gqa::Plan& P = h->plan;
   size_t off = 0;
@@ -129,6 +135,10 @@ size_t plan_layout(gqa_attn* h) {
   off = align_up(off + P.wide.size() * sizeof(gqa::WorkItem), 256);
   h->off_narrow = off;
   off = align_up(off + P.narrow.size() * sizeof(gqa::WorkItem), 256);
+  h->off_wide_bins = off;
+  off = align_up(off + P.wide_bins.size() * sizeof(int32_t), 256);
+  h->off_narrow_bins = off;
+  off = align_up(off + P.narrow_bins.size() * sizeof(int32_t), 256);
   h->off_units = off;
   off = align_up(off + P.units.size() * sizeof(gqa::UnitDesc), 256);
   h->off_branches = off;
@@ -171,6 +181,8 @@ gqa_status upload_plan(gqa_attn* h, hipStream_t stream) {
   };
   put(h->off_wide, P.wide.data(), P.wide.size() * sizeof(gqa::WorkItem));
   put(h->off_narrow, P.narrow.data(), P.narrow.size() * sizeof(gqa::WorkItem));
+  put(h->off_wide_bins, P.wide_bins.data(), P.wide_bins.size() * sizeof(int32_t));
+  put(h->off_narrow_bins, P.narrow_bins.data(), P.narrow_bins.size() * sizeof(int32_t));
   put(h->off_units, P.units.data(), P.units.size() * sizeof(gqa::UnitDesc));
   put(h->off_branches, P.branches.data(), P.branches.size() * sizeof(gqa::BranchDesc));
   put(h->off_tiles, P.tiles.data(), P.tiles.size() * sizeof(gqa::TileInfo));
@@ -237,6 +249,12 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out) {
   if (h->p.softmax_scale <= 0.f) h->p.softmax_scale = 1.0f / std::sqrt((float)p->head_dim);
   h->device = dev;
   h->n_cu = ncu > 0 ? ncu : 256;
+  e = gqa::attention_occupancy(h->p.dtype, h->p.head_dim, false, &h->wide_per_cu);
+  if (e == hipSuccess) e = gqa::attention_occupancy(h->p.dtype, h->p.head_dim, true, &h->narrow_per_cu);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  }
   *out = h;
   return GQA_OK;
 }
@@ -266,7 +284,7 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   gqa::PlanInput in;
   gqa_status s = make_input(&h->p, n_groups, group_shared_start, group_shared_len, n_branches,
                             branch_group, branch_q_len, branch_private_len, splits_override, causal,
-                            h->n_cu, &in);
+                            h->n_cu, h->wide_per_cu, h->narrow_per_cu, &in);
   if (s != GQA_OK) return s;
 
   // Plan cache key: every input of the planner.
@@ -365,12 +383,16 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   }
   if (!Q.wide.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
-    e = gqa::launch_attention(a, (int32_t)Q.wide.size(), false, h->p.dtype, h->p.head_dim, st, ev(0), ev(1));
+    a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
+                              ev(1));
     if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
   }
   if (!Q.narrow.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
-    e = gqa::launch_attention(a, (int32_t)Q.narrow.size(), true, h->p.dtype, h->p.head_dim, st, ev(2), ev(3));
+    a.bins = (const int32_t*)(h->d_plan + h->off_narrow_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, st, ev(2),
+                              ev(3));
     if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
   }
   if (Q.merge_rows > 0) {
@@ -435,7 +457,7 @@ gqa_status gqa_attn_plan_host(const gqa_attn_params* p, int32_t n_groups, const 
   if (s != GQA_OK) return s;
   gqa::PlanInput in;
   s = make_input(p, n_groups, group_shared_start, group_shared_len, n_branches, branch_group, branch_q_len,
-                 branch_private_len, splits_override, causal, 256, &in);
+                 branch_private_len, splits_override, causal, 256, 1, 1, &in);
   if (s != GQA_OK) return s;
   gqa::Plan P;
   std::string err = gqa::build_plan(in, &P);
@@ -444,12 +466,18 @@ gqa_status gqa_attn_plan_host(const gqa_attn_params* p, int32_t n_groups, const 
   if (n_items) *n_items = n;
   if (items && cap >= n) {
     int64_t k = 0;
-    for (int pass = 0; pass < 2; ++pass)
-      for (const gqa::WorkItem& w : (pass == 0 ? P.wide : P.narrow)) {
-        int32_t* r = items + 8 * k++;
+    for (int pass = 0; pass < 2; ++pass) {
+      const std::vector<gqa::WorkItem>& list = (pass == 0) ? P.wide : P.narrow;
+      const std::vector<int32_t>& bins = (pass == 0) ? P.wide_bins : P.narrow_bins;
+      int32_t b = 0;
+      for (size_t x = 0; x < list.size(); ++x) {
+        while (bins[b + 1] <= (int32_t)x) ++b;
+        const gqa::WorkItem& w = list[x];
+        int32_t* r = items + 9 * k++;
         r[0] = P.unit_slot[w.unit]; r[1] = w.kv; r[2] = w.row_begin; r[3] = w.n_rows;
-        r[4] = w.key_begin; r[5] = w.key_end; r[6] = w.split; r[7] = pass;
+        r[4] = w.key_begin; r[5] = w.key_end; r[6] = w.split; r[7] = pass; r[8] = b;
       }
+    }
   }
   if (splits) std::memcpy(splits, P.api_splits.data(), sizeof(int32_t) * P.api_splits.size());
   if (stats) fill_stats(P, p->head_dim, stats);

@@ -512,40 +512,45 @@ __global__ void __launch_bounds__(256, (Cfg<T, D, false>::WAVES_PER_SIMD))
 attn_wide(AttnArgs a) {
   using C = Cfg<T, D, false>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  const WorkItem it = a.items[blockIdx.x];
-  const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
-  const int rloc = wave * 32 + i;
-  const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
-  State<C> s;
-  load_q<C, T, D>(a, w, it.kv, h, s);
-  int pmin, pmax;
-  wave_pos_range(w, &pmin, &pmax);
-  const bool wave_rows = wave * 32 < it.n_rows;
-  const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
+  const int bin_end = a.bins[blockIdx.x + 1];
+  for (int idx = a.bins[blockIdx.x]; idx < bin_end; ++idx) {
+    // The previous item's last tile loop iteration ended with a barrier after
+    // all LDS reads, so its stages may be refilled at once.
+    const WorkItem it = a.items[idx];
+    const UnitDesc u = a.units[it.unit];
+    const int rloc = wave * 32 + i;
+    const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
+    State<C> s;
+    load_q<C, T, D>(a, w, it.kv, h, s);
+    int pmin, pmax;
+    wave_pos_range(w, &pmin, &pmax);
+    const bool wave_rows = wave * 32 < it.n_rows;
+    const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
 
-  const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;
-  Stage<C> st;
-  load_tile<C, T, D>(src, it.key_begin, it.key_end, tid, st);
-  store_tile<C, T, D>((T*)smem, (T*)(smem + C::K_ELEMS * sizeof(T)), tid, st);
-  __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    const bool more = j + 1 < nt;
-    if (more) load_tile<C, T, D>(src, it.key_begin + (j + 1) * C::BN, it.key_end, tid, st);
-    const int tk0 = it.key_begin + j * C::BN;       // unit-local first key of the tile
-    const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
-    if (wave_rows && !future) {
-      char* stg = smem + (j & 1) * C::STAGE;
-      run_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, u, tk0, it.key_end,
-                        a.causal, w.pos, pmin, a.scale_log2, i, h);
-    }
-    if (more) {
-      char* stg = smem + ((j + 1) & 1) * C::STAGE;
-      store_tile<C, T, D>((T*)stg, (T*)(stg + C::K_ELEMS * sizeof(T)), tid, st);
-    }
+    const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;
+    Stage<C> st;
+    load_tile<C, T, D>(src, it.key_begin, it.key_end, tid, st);
+    store_tile<C, T, D>((T*)smem, (T*)(smem + C::K_ELEMS * sizeof(T)), tid, st);
     __syncthreads();
+    for (int j = 0; j < nt; ++j) {
+      const bool more = j + 1 < nt;
+      if (more) load_tile<C, T, D>(src, it.key_begin + (j + 1) * C::BN, it.key_end, tid, st);
+      const int tk0 = it.key_begin + j * C::BN;       // unit-local first key of the tile
+      const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
+      if (wave_rows && !future) {
+        char* stg = smem + (j & 1) * C::STAGE;
+        run_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, u, tk0, it.key_end,
+                          a.causal, w.pos, pmin, a.scale_log2, i, h);
+      }
+      if (more) {
+        char* stg = smem + ((j + 1) & 1) * C::STAGE;
+        store_tile<C, T, D>((T*)stg, (T*)(stg + C::K_ELEMS * sizeof(T)), tid, st);
+      }
+      __syncthreads();
+    }
+    write_row<C, T, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
   }
-  write_row<C, T, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
 }
 
 // ------------------------------------------------------ wide, bf16, DMA ----
@@ -727,9 +732,11 @@ __device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const D
 // of the wave sees a score more than 2^8 above it; otherwise p = 2^(s*c - m)
 // stays below 256, which bf16 P and fp32 O, l hold exactly as well as
 // smaller values. The result is the same softmax; only the reference point
-// of the exponent differs between rescales. The exponentials of each 32-key
-// half are computed right before that half's P.V products, so the second
-// half's VALU work overlaps the first half's MFMAs.
+// of the exponent differs between rescales. The P.V products are software
+// pipelined in 16-key chunks: the exponentials and the V^T operand reads of
+// chunk n + 1 are issued between chunk n's MFMAs (scheduling fences keep
+// the compiler from regrouping them), so the softmax VALU work runs in the
+// matrix core's shadow.
 template <class C, int D, bool MASK>
 __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const DmaLane<C>& L,
                                             State<C>& s, int kpos0, int n_valid, int causal,
@@ -789,37 +796,46 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
     s.m = m_new;
   }
   const float neg_m = (s.m == kNegInf) ? 0.f : -s.m;
-  float rs = 0.f;
+  // Chunk n = 16 keys of the tile (S^T block n / 2, accumulator entries
+  // 8 (n % 2) .. +7 of this lane).
+  constexpr int NCH = 2 * C::SB;
+  float r0 = 0.f, r1 = 0.f;
+  bf16x8_t pb[2];
+  auto make_p = [&](int n, bf16x8_t& out) {
+    const int kb = n >> 1, r = 8 * (n & 1);
 #pragma unroll
-  for (int kb = 0; kb < C::SB; ++kb) {
-    float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r], c, neg_m));
-      const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + 1], c, neg_m));
-      sacc[kb][r] = p0;
-      sacc[kb][r + 1] = p1;
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][r + e], c, neg_m));
+      const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][r + e + 1], c, neg_m));
       r0 += p0;
       r1 += p1;
+      out[e] = (__bf16)p0;
+      out[e + 1] = (__bf16)p1;
     }
-    rs += r0 + r1;
+  };
+  auto v_frag = [&](int n, int db) -> bf16x8_t {
+    const uint32_t va = vbs[db] + (16 * n) * C::ROW;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)va);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)(va + 8 * C::ROW));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8_t vf[C::OB];
+  make_p(0, pb[0]);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      bf16x8_t pb;
+  for (int db = 0; db < C::OB; ++db) vf[db] = v_frag(0, db);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][8 * cc + e];
-      const int krow = (16 * (2 * kb + cc)) * C::ROW;
+  for (int n = 0; n < NCH; ++n) {
+    const int cur = n & 1;
 #pragma unroll
-      for (int db = 0; db < C::OB; ++db) {
-        const uint32_t va = vbs[db] + krow;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)va);
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(uintptr_t)(va + 8 * C::ROW));
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        s.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, s.o[db], 0, 0, 0);
-      }
+    for (int db = 0; db < C::OB; ++db) {
+      s.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[cur], s.o[db], 0, 0, 0);
+      if (n + 1 < NCH) vf[db] = v_frag(n + 1, db);
+      if (db == 1 && n + 1 < NCH) make_p(n + 1, pb[cur ^ 1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  s.l += rs;   // sum over this lane's keys; the two halves are added once, at the end
+  s.l += r0 + r1;   // sum over this lane's keys; the two halves are added once, at the end
 }
 
 template <class C, int D>
@@ -852,49 +868,55 @@ attn_wide_dma(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char v2[C::TB];
   __shared__ __attribute__((aligned(1024))) char k3[C::TB];
   __shared__ __attribute__((aligned(1024))) char v3[C::TB];
-  const WorkItem it = a.items[blockIdx.x];
-  const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
-  const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
   const DmaLane<C> L = dma_lane<C>(wave, lane);
-  const int kb0 = it.key_begin, ke = it.key_end;
-  const int nt = (ke - kb0 + C::BN - 1) / C::BN;
-  // The first pair's DMA goes out before the row bookkeeping and Q loads.
-  dma_tile_any<C, D>(src, L, wave, kb0, ke, k0, v0);
-  if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
-  const int rloc = wave * 32 + i;
-  const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
-  State<C> s;
-  load_q<C, uint16_t, D>(a, w, it.kv, h, s);
-  int pmin, pmax;
-  wave_pos_range(w, &pmin, &pmax);
-  const bool active = wave * 32 < it.n_rows;
-  const float c = a.scale_log2;
-#define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                              \
-  {                                                                                                   \
-    wait_dma<0>();                                                                                    \
-    lds_barrier();                                                                                    \
-    if (j + 2 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);              \
-    if (j + 3 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);              \
-    dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,  \
-                active, c, i, h);                                                                     \
-    if (j + 1 < nt)                                                                                   \
-      dma_step<C, D>(lds_u32(KB), lds_u32(VB), L, s, u, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin, \
-                  pmax, active, c, i, h);                                                             \
-  }
-  for (int j0 = 0; j0 < nt; j0 += 4) {
-    {
-      const int j = j0;
-      GQA_DMA_PAIR(k0, v0, k1, v1, k2, v2, k3, v3)
+  const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
+  for (int idx = bin_begin; idx < bin_end; ++idx) {
+    // Every wave has finished reading the previous item's ring before its
+    // stages are refilled.
+    if (idx > bin_begin) lds_barrier();
+    const WorkItem it = a.items[idx];
+    const UnitDesc u = a.units[it.unit];
+    const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+    const int kb0 = it.key_begin, ke = it.key_end;
+    const int nt = (ke - kb0 + C::BN - 1) / C::BN;
+    // The first pair's DMA goes out before the row bookkeeping and Q loads.
+    dma_tile_any<C, D>(src, L, wave, kb0, ke, k0, v0);
+    if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
+    const int rloc = wave * 32 + i;
+    const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
+    State<C> s;
+    load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+    int pmin, pmax;
+    wave_pos_range(w, &pmin, &pmax);
+    const bool active = wave * 32 < it.n_rows;
+    const float c = a.scale_log2;
+#define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                                    \
+    {                                                                                                       \
+      wait_dma<0>();                                                                                        \
+      lds_barrier();                                                                                        \
+      if (j + 2 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);                \
+      if (j + 3 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);                \
+      dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,   \
+                  active, c, i, h);                                                                         \
+      if (j + 1 < nt)                                                                                       \
+        dma_step<C, D>(lds_u32(KB), lds_u32(VB), L, s, u, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin, \
+                    pmax, active, c, i, h);                                                                 \
     }
-    if (j0 + 2 < nt) {
-      const int j = j0 + 2;
-      GQA_DMA_PAIR(k2, v2, k3, v3, k0, v0, k1, v1)
+    for (int j0 = 0; j0 < nt; j0 += 4) {
+      {
+        const int j = j0;
+        GQA_DMA_PAIR(k0, v0, k1, v1, k2, v2, k3, v3)
+      }
+      if (j0 + 2 < nt) {
+        const int j = j0 + 2;
+        GQA_DMA_PAIR(k2, v2, k3, v3, k0, v0, k1, v1)
+      }
     }
-  }
 #undef GQA_DMA_PAIR
-  s.l += __shfl_xor(s.l, 32);
-  write_row<C, uint16_t, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
+    s.l += __shfl_xor(s.l, 32);
+    write_row<C, uint16_t, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
+  }
 }
 
 // -------------------------------------------------------------- narrow ----
@@ -903,72 +925,78 @@ __global__ void __launch_bounds__(256, (Cfg<T, D, true>::WAVES_PER_SIMD))
 attn_narrow(AttnArgs a) {
   using C = Cfg<T, D, true>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  const WorkItem it = a.items[blockIdx.x];
-  const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
-  const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
-  State<C> s;
-  load_q<C, T, D>(a, w, it.kv, h, s);
-  int pmin, pmax;
-  wave_pos_range(w, &pmin, &pmax);
-  const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
+  const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
+  for (int idx = bin_begin; idx < bin_end; ++idx) {
+    // Every wave has read the previous item's merge exchange before the
+    // stages are refilled.
+    if (idx > bin_begin) __syncthreads();
+    const WorkItem it = a.items[idx];
+    const UnitDesc u = a.units[it.unit];
+    const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+    State<C> s;
+    load_q<C, T, D>(a, w, it.kv, h, s);
+    int pmin, pmax;
+    wave_pos_range(w, &pmin, &pmax);
+    const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
 
-  const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;   // wave tiles: wave w takes w, w+4, ...
-  const int rounds = (nt + 3) / 4;
-  char* stg = smem + wave * C::STAGE;
-  T* Ks = (T*)stg;
-  T* Vs = (T*)(stg + C::K_ELEMS * sizeof(T));
-  Stage<C> st;
-  if (wave < nt) load_tile<C, T, D>(src, it.key_begin + wave * C::BN, it.key_end, lane, st);
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int j = wave + 4 * rd;
-    const bool have = j < nt;
-    if (have) store_tile<C, T, D>(Ks, Vs, lane, st);
-    __syncthreads();
-    if (j + 4 < nt) load_tile<C, T, D>(src, it.key_begin + (j + 4) * C::BN, it.key_end, lane, st);
-    if (have) {
-      const int tk0 = it.key_begin + j * C::BN;
-      const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
-      if (!future)
-        run_tile<C, T, D>(Ks, Vs, s, u, tk0, it.key_end, a.causal, w.pos, pmin, a.scale_log2, i, h);
+    const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;   // wave tiles: wave w takes w, w+4, ...
+    const int rounds = (nt + 3) / 4;
+    char* stg = smem + wave * C::STAGE;
+    T* Ks = (T*)stg;
+    T* Vs = (T*)(stg + C::K_ELEMS * sizeof(T));
+    Stage<C> st;
+    if (wave < nt) load_tile<C, T, D>(src, it.key_begin + wave * C::BN, it.key_end, lane, st);
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int j = wave + 4 * rd;
+      const bool have = j < nt;
+      if (have) store_tile<C, T, D>(Ks, Vs, lane, st);
+      __syncthreads();
+      if (j + 4 < nt) load_tile<C, T, D>(src, it.key_begin + (j + 4) * C::BN, it.key_end, lane, st);
+      if (have) {
+        const int tk0 = it.key_begin + j * C::BN;
+        const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
+        if (!future)
+          run_tile<C, T, D>(Ks, Vs, s, u, tk0, it.key_end, a.causal, w.pos, pmin, a.scale_log2, i, h);
+      }
+      __syncthreads();
     }
+    // Merge the four waves' states (same rows, disjoint keys) through LDS.
+    float* mo = (float*)smem;                       // [wave][db][r][lane]
+    float2* mml = (float2*)(smem + 4 * C::OB * 16 * 64 * 4);
+#pragma unroll
+    for (int db = 0; db < C::OB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
+    mml[wave * 64 + lane] = make_float2(s.m, s.l);
     __syncthreads();
-  }
-  // Merge the four waves' states (same rows, disjoint keys) through LDS.
-  float* mo = (float*)smem;                       // [wave][db][r][lane]
-  float2* mml = (float2*)(smem + 4 * C::OB * 16 * 64 * 4);
+    float mk[4], lk[4];
+    float M = kNegInf;
 #pragma unroll
-  for (int db = 0; db < C::OB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
-  mml[wave * 64 + lane] = make_float2(s.m, s.l);
-  __syncthreads();
-  float mk[4], lk[4];
-  float M = kNegInf;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float2 x = mml[k * 64 + lane];
-    mk[k] = x.x;
-    lk[k] = x.y;
-    M = fmaxf(M, x.x);
-  }
-  const float M_use = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, wk[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    wk[k] = exp2_fast(mk[k] - M_use);
-    L += lk[k] * wk[k];
-  }
-  for (int db = wave; db < C::OB; db += 4) {
-    f32x16_t acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
-      acc[r] = x;
+    for (int k = 0; k < 4; ++k) {
+      const float2 x = mml[k * 64 + lane];
+      mk[k] = x.x;
+      lk[k] = x.y;
+      M = fmaxf(M, x.x);
     }
-    write_row<C, T, D>(a, it, u, w, M, L, &acc, db, db + 1, wave == 0, h);
+    const float M_use = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, wk[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      wk[k] = exp2_fast(mk[k] - M_use);
+      L += lk[k] * wk[k];
+    }
+    for (int db = wave; db < C::OB; db += 4) {
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
+        acc[r] = x;
+      }
+      write_row<C, T, D>(a, it, u, w, M, L, &acc, db, db + 1, wave == 0, h);
+    }
   }
 }
 
@@ -999,87 +1027,93 @@ attn_narrow_dma(AttnArgs a) {
   using C = NarrowDmaCfg<D>;
   __shared__ __attribute__((aligned(1024))) char st0[4 * 2 * C::TB];   // per wave: K tile then V tile
   __shared__ __attribute__((aligned(1024))) char st1[4 * 2 * C::TB];
-  const WorkItem it = a.items[blockIdx.x];
-  const UnitDesc u = a.units[it.unit];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
-  const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
   const DmaLane<C> L = dma_lane<C>(0, lane);
-  const int kb0 = it.key_begin, ke = it.key_end, causal = a.causal;
-  const int nt = (ke - kb0 + C::BN - 1) / C::BN;
-  constexpr int VM = 2 * C::NINST;
-  char* K0 = st0 + wave * 2 * C::TB;
-  char* V0 = K0 + C::TB;
-  char* K1 = st1 + wave * 2 * C::TB;
-  char* V1 = K1 + C::TB;
-  // The first tiles' DMA goes out before the row bookkeeping and Q loads,
-  // whose dependent lookups would otherwise delay it.
-  if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
-  if (wave + 4 < nt) dma_tile_any<C, D>(src, L, 0, kb0 + (wave + 4) * C::BN, ke, K1, V1);
-  const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
-  State<C> s;
-  load_q<C, uint16_t, D>(a, w, it.kv, h, s);
-  int pmin, pmax;
-  wave_pos_range(w, &pmin, &pmax);
-  const bool active = it.n_rows > 0;
-  const float c = a.scale_log2;
-  for (int j = wave; j < nt; j += 8) {
-    if (j + 4 < nt) wait_dma<VM>();
-    else wait_dma<0>();
-    dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, u, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
-                   i, h);
-    if (j + 8 < nt) {
-      wait_dma<63>();   // own LDS reads of stage 0 done
-      dma_tile_any<C, D>(src, L, 0, kb0 + (j + 8) * C::BN, ke, K0, V0);
+  const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
+  for (int idx = bin_begin; idx < bin_end; ++idx) {
+    // Every wave has read the previous item's merge exchange before the
+    // stages are refilled.
+    if (idx > bin_begin) __syncthreads();
+    const WorkItem it = a.items[idx];
+    const UnitDesc u = a.units[it.unit];
+    const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+    const int kb0 = it.key_begin, ke = it.key_end, causal = a.causal;
+    const int nt = (ke - kb0 + C::BN - 1) / C::BN;
+    constexpr int VM = 2 * C::NINST;
+    char* K0 = st0 + wave * 2 * C::TB;
+    char* V0 = K0 + C::TB;
+    char* K1 = st1 + wave * 2 * C::TB;
+    char* V1 = K1 + C::TB;
+    // The first tiles' DMA goes out before the row bookkeeping and Q loads,
+    // whose dependent lookups would otherwise delay it.
+    if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
+    if (wave + 4 < nt) dma_tile_any<C, D>(src, L, 0, kb0 + (wave + 4) * C::BN, ke, K1, V1);
+    const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+    State<C> s;
+    load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+    int pmin, pmax;
+    wave_pos_range(w, &pmin, &pmax);
+    const bool active = it.n_rows > 0;
+    const float c = a.scale_log2;
+    for (int j = wave; j < nt; j += 8) {
+      if (j + 4 < nt) wait_dma<VM>();
+      else wait_dma<0>();
+      dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, u, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
+                     i, h);
+      if (j + 8 < nt) {
+        wait_dma<63>();   // own LDS reads of stage 0 done
+        dma_tile_any<C, D>(src, L, 0, kb0 + (j + 8) * C::BN, ke, K0, V0);
+      }
+      const int j2 = j + 4;
+      if (j2 >= nt) break;
+      if (j2 + 4 < nt) wait_dma<VM>();
+      else wait_dma<0>();
+      dma_step<C, D>(lds_u32(K1), lds_u32(V1), L, s, u, kb0 + j2 * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
+                     i, h);
+      if (j2 + 8 < nt) {
+        wait_dma<63>();
+        dma_tile_any<C, D>(src, L, 0, kb0 + (j2 + 8) * C::BN, ke, K1, V1);
+      }
     }
-    const int j2 = j + 4;
-    if (j2 >= nt) break;
-    if (j2 + 4 < nt) wait_dma<VM>();
-    else wait_dma<0>();
-    dma_step<C, D>(lds_u32(K1), lds_u32(V1), L, s, u, kb0 + j2 * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
-                   i, h);
-    if (j2 + 8 < nt) {
-      wait_dma<63>();
-      dma_tile_any<C, D>(src, L, 0, kb0 + (j2 + 8) * C::BN, ke, K1, V1);
+    // Merge the four waves' states (same rows, disjoint keys) through LDS.
+    s.l += __shfl_xor(s.l, 32);
+    wait_dma<0>();
+    __syncthreads();
+    float* mo = (float*)st0;                       // [wave][db][r][lane]
+    float2* mml = (float2*)st1;
+#pragma unroll
+    for (int db = 0; db < C::OB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
+    mml[wave * 64 + lane] = make_float2(s.m, s.l);
+    __syncthreads();
+    float mk[4], lk[4];
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 x = mml[k * 64 + lane];
+      mk[k] = x.x;
+      lk[k] = x.y;
+      M = fmaxf(M, x.x);
     }
-  }
-  // Merge the four waves' states (same rows, disjoint keys) through LDS.
-  s.l += __shfl_xor(s.l, 32);
-  wait_dma<0>();
-  __syncthreads();
-  float* mo = (float*)st0;                       // [wave][db][r][lane]
-  float2* mml = (float2*)st1;
+    const float M_use = (M == kNegInf) ? 0.f : M;
+    float Lsum = 0.f, wk[4];
 #pragma unroll
-  for (int db = 0; db < C::OB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
-  mml[wave * 64 + lane] = make_float2(s.m, s.l);
-  __syncthreads();
-  float mk[4], lk[4];
-  float M = kNegInf;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float2 x = mml[k * 64 + lane];
-    mk[k] = x.x;
-    lk[k] = x.y;
-    M = fmaxf(M, x.x);
-  }
-  const float M_use = (M == kNegInf) ? 0.f : M;
-  float Lsum = 0.f, wk[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    wk[k] = exp2_fast(mk[k] - M_use);
-    Lsum += lk[k] * wk[k];
-  }
-  for (int db = wave; db < C::OB; db += 4) {
-    f32x16_t acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
-      acc[r] = x;
+    for (int k = 0; k < 4; ++k) {
+      wk[k] = exp2_fast(mk[k] - M_use);
+      Lsum += lk[k] * wk[k];
     }
-    write_row<C, uint16_t, D>(a, it, u, w, M, Lsum, &acc, db, db + 1, wave == 0, h);
+    for (int db = wave; db < C::OB; db += 4) {
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
+        acc[r] = x;
+      }
+      write_row<C, uint16_t, D>(a, it, u, w, M, Lsum, &acc, db, db + 1, wave == 0, h);
+    }
   }
 }
 
@@ -1160,18 +1194,36 @@ lse_merge(AttnArgs a) {
   hipExtLaunchKernelGGL(KERNEL, dim3(GRID), dim3(BLOCK), 0, st, e0, e1, 0, a)
 
 template <typename T, int D>
-hipError_t launch_attn_t(const AttnArgs& a, int32_t n_items, bool narrow, hipStream_t st, hipEvent_t e0,
+hipError_t launch_attn_t(const AttnArgs& a, int32_t n_bins, bool narrow, hipStream_t st, hipEvent_t e0,
                          hipEvent_t e1) {
-  if (n_items <= 0) return hipSuccess;
+  if (n_bins <= 0) return hipSuccess;
   if (narrow) {
-    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_items, 256);
-    else GQA_LAUNCH((attn_narrow<T, D>), n_items, 256);
+    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_bins, 256);
+    else GQA_LAUNCH((attn_narrow<T, D>), n_bins, 256);
   } else if constexpr (std::is_same<T, uint16_t>::value) {
-    GQA_LAUNCH((attn_wide_dma<D>), n_items, 512);
+    GQA_LAUNCH((attn_wide_dma<D>), n_bins, 512);
   } else {
-    GQA_LAUNCH((attn_wide<T, D>), n_items, 256);
+    GQA_LAUNCH((attn_wide<T, D>), n_bins, 256);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t occupancy_t(bool narrow, int* per_cu) {
+  int n = 0;
+  hipError_t e;
+  if (narrow) {
+    if constexpr (std::is_same<T, uint16_t>::value)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow_dma<D>, 256, 0);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow<T, D>, 256, 0);
+  } else if constexpr (std::is_same<T, uint16_t>::value) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_wide_dma<D>, 512, 0);
+  } else {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_wide<T, D>, 256, 0);
+  }
+  *per_cu = n > 0 ? n : 1;
+  return e;
 }
 
 // U = partials whose loads a thread issues before folding them: as many as
@@ -1190,14 +1242,20 @@ hipError_t launch_merge_t(const AttnArgs& a, int max_parts, hipStream_t st, hipE
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int dtype, int head_dim,
+hipError_t launch_attention(const AttnArgs& a, int32_t n_bins, bool narrow, int dtype, int head_dim,
                             hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (dtype == 0) {
-    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, n_items, narrow, stream, ev_start, ev_stop);
-    return launch_attn_t<uint16_t, 64>(a, n_items, narrow, stream, ev_start, ev_stop);
+    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, n_bins, narrow, stream, ev_start, ev_stop);
+    return launch_attn_t<uint16_t, 64>(a, n_bins, narrow, stream, ev_start, ev_stop);
   }
-  if (head_dim == 128) return launch_attn_t<float, 128>(a, n_items, narrow, stream, ev_start, ev_stop);
-  return launch_attn_t<float, 64>(a, n_items, narrow, stream, ev_start, ev_stop);
+  if (head_dim == 128) return launch_attn_t<float, 128>(a, n_bins, narrow, stream, ev_start, ev_stop);
+  return launch_attn_t<float, 64>(a, n_bins, narrow, stream, ev_start, ev_stop);
+}
+
+hipError_t attention_occupancy(int dtype, int head_dim, bool narrow, int* per_cu) {
+  if (dtype == 0) return head_dim == 128 ? occupancy_t<uint16_t, 128>(narrow, per_cu)
+                                         : occupancy_t<uint16_t, 64>(narrow, per_cu);
+  return head_dim == 128 ? occupancy_t<float, 128>(narrow, per_cu) : occupancy_t<float, 64>(narrow, per_cu);
 }
 
 hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream,

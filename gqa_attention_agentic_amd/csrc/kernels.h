@@ -15,6 +15,7 @@ struct AttnArgs {
   const void* v_pages;
   const int32_t* page_table;
   const WorkItem* items;
+  const int32_t* bins;  // workgroup b runs items [bins[b], bins[b+1])
   const UnitDesc* units;
   const BranchDesc* branches;
   const TileInfo* tiles;
@@ -36,12 +37,17 @@ struct AttnArgs {
   int32_t pad;
 };
 
-// Attention over a work-item list. narrow selects the 32-row kernel.
+// Attention over a work-item list: one workgroup per bin (a.bins holds
+// n_bins + 1 offsets into a.items). narrow selects the 32-row kernel.
 // ev_start / ev_stop (may be null) are recorded by the launch itself around
 // the kernel's execution (hipExtLaunchKernelGGL), for kernel-only timing.
-hipError_t launch_attention(const AttnArgs& a, int32_t n_items, bool narrow, int dtype,
+hipError_t launch_attention(const AttnArgs& a, int32_t n_bins, bool narrow, int dtype,
                             int head_dim, hipStream_t stream, hipEvent_t ev_start = nullptr,
                             hipEvent_t ev_stop = nullptr);
+
+// Workgroups of the attention kernel for (dtype, head_dim, narrow) that stay
+// resident on one CU at once (at least 1).
+hipError_t attention_occupancy(int dtype, int head_dim, bool narrow, int* per_cu);
 
 // Log-sum-exp merge of the partials of every output row with >= 2 of them.
 // max_parts: the largest number of partials any output row has.

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <functional>
 #include <limits>
+#include <map>
 #include <queue>
 
 namespace gqa {
@@ -62,59 +63,97 @@ double lpt_makespan(std::vector<double> cost, int slots) {
   return mk;
 }
 
-// Workgroups are dealt to the 8 XCDs of the chip round-robin by launch
-// index, and each XCD has its own L2. Items that read the same KV range
-// (same unit, KV head and shard; different M-tiles) are therefore put on
-// launch indices of one residue mod 8, next to each other, so their K/V
-// tiles are fetched into one L2 once. Groups go to the least-loaded XCD,
-// largest first; each XCD's queue keeps the largest-first order.
+// Fixed cost of an item in key units (descriptor and Q loads, the first
+// tile's latency, the partial write-back): about one and a half 64-key tiles.
+constexpr double kItemFixedKeys = 96.0;
 constexpr int kXcds = 8;
 
-void xcd_order(std::vector<WorkItem>* items, int n_cu) {
-  if (items->size() < (size_t)2 * kXcds || n_cu % kXcds != 0) return;
-  struct Group { std::vector<WorkItem> v; int64_t cost = 0; };
-  std::vector<Group> groups;
-  {
-    std::vector<std::pair<std::array<int32_t, 3>, size_t>> keyed;
-    std::vector<std::array<int32_t, 3>> keys;
-    for (const WorkItem& w : *items) {
-      const std::array<int32_t, 3> k{w.unit, w.kv, w.split};
-      size_t gi = 0;
-      for (; gi < keys.size(); ++gi)
-        if (keys[gi] == k) break;
-      if (gi == keys.size()) {
-        keys.push_back(k);
-        groups.emplace_back();
+double item_cost(const WorkItem& w) { return (double)(w.key_end - w.key_begin) + kItemFixedKeys; }
+
+// List scheduling of items (visited in `order`, largest first) onto `nb`
+// bins: each goes to the least-loaded bin. Returns the largest bin load.
+double lpt_assign(const std::vector<double>& cost, const std::vector<size_t>& order, int nb,
+                  std::vector<int>* bin_of) {
+  typedef std::pair<double, int> Slot;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int b = 0; b < nb; ++b) heap.push(Slot(0.0, b));
+  double mk = 0.0;
+  for (size_t i : order) {
+    Slot s = heap.top();
+    heap.pop();
+    (*bin_of)[i] = s.second;
+    s.first += cost[i];
+    mk = std::max(mk, s.first);
+    heap.push(s);
+  }
+  return mk;
+}
+
+// Packs a kernel's items (sorted largest first) into at most `slots` bins,
+// one per resident workgroup, so that every workgroup starts at once and
+// runs its bin's items back to back; the hardware then never has to queue a
+// workgroup behind a long one.
+//
+// Workgroups are dealt to the 8 XCDs of the chip round-robin by launch
+// index and each XCD has its own L2, so bin b runs on XCD b % 8. Items that
+// read the same KV range (same unit, KV head and shard; different M-tiles)
+// are kept on one XCD, so their K/V tiles are fetched into one L2 once:
+// such groups go to the least-loaded XCD, largest first, and each XCD's
+// items to its least-loaded bins. That placement is kept unless plain list
+// scheduling over all bins would finish more than 2% sooner.
+void bin_items(std::vector<WorkItem>* items, int slots, int n_cu, std::vector<int32_t>* bins) {
+  const size_t n = items->size();
+  bins->assign(1, 0);
+  if (n == 0) return;
+  const int nb = (int)std::min<int64_t>((int64_t)n, std::max(1, slots));
+  std::vector<double> cost(n);
+  std::vector<size_t> order(n);
+  for (size_t i = 0; i < n; ++i) {
+    cost[i] = item_cost((*items)[i]);
+    order[i] = i;
+  }
+  std::vector<int> bin_of(n, 0);
+  const double mk_plain = lpt_assign(cost, order, nb, &bin_of);
+  if (n_cu % kXcds == 0 && nb % kXcds == 0 && nb >= 2 * kXcds) {
+    const int per = nb / kXcds;
+    std::map<std::array<int32_t, 3>, size_t> gid;
+    std::vector<std::vector<size_t>> members;
+    std::vector<double> gcost;
+    for (size_t i = 0; i < n; ++i) {
+      const WorkItem& w = (*items)[i];
+      auto ins = gid.emplace(std::array<int32_t, 3>{w.unit, w.kv, w.split}, members.size());
+      if (ins.second) {
+        members.emplace_back();
+        gcost.push_back(0.0);
       }
-      groups[gi].v.push_back(w);
-      groups[gi].cost += (int64_t)(w.key_end - w.key_begin) + 96;
+      members[ins.first->second].push_back(i);
+      gcost[ins.first->second] += cost[i];
+    }
+    std::vector<size_t> gorder(members.size());
+    for (size_t g = 0; g < gorder.size(); ++g) gorder[g] = g;
+    std::stable_sort(gorder.begin(), gorder.end(), [&](size_t a, size_t b) { return gcost[a] > gcost[b]; });
+    std::vector<int> xcd_of(members.size(), 0);
+    lpt_assign(gcost, gorder, kXcds, &xcd_of);
+    std::vector<std::vector<size_t>> on_xcd(kXcds);
+    for (size_t i = 0; i < n; ++i) {
+      const WorkItem& w = (*items)[i];
+      on_xcd[xcd_of[gid[std::array<int32_t, 3>{w.unit, w.kv, w.split}]]].push_back(i);   // index order = largest first
+    }
+    std::vector<int> local(n, 0);
+    double mk_xcd = 0.0;
+    for (int x = 0; x < kXcds; ++x) mk_xcd = std::max(mk_xcd, lpt_assign(cost, on_xcd[x], per, &local));
+    if (mk_xcd <= mk_plain * 1.02) {
+      for (int x = 0; x < kXcds; ++x)
+        for (size_t i : on_xcd[x]) bin_of[i] = local[i] * kXcds + x;
     }
   }
-  std::stable_sort(groups.begin(), groups.end(),
-                   [](const Group& a, const Group& b) { return a.cost > b.cost; });
-  std::vector<std::vector<WorkItem>> q(kXcds);
-  std::vector<int64_t> load(kXcds, 0);
-  for (const Group& g : groups) {
-    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-    q[x].insert(q[x].end(), g.v.begin(), g.v.end());
-    load[x] += g.cost;
-  }
-  std::vector<size_t> head(kXcds, 0);
-  size_t done = 0;
-  std::vector<WorkItem> out;
-  out.reserve(items->size());
-  while (done < items->size()) {
-    for (int x = 0; x < kXcds && done < items->size(); ++x) {
-      int src = x;
-      if (head[src] == q[src].size()) {   // this XCD's queue ran dry: take from the fullest
-        size_t best = 0;
-        for (int y = 0; y < kXcds; ++y)
-          if (q[y].size() - head[y] > best) { best = q[y].size() - head[y]; src = y; }
-      }
-      out.push_back(q[src][head[src]++]);
-      ++done;
-    }
-  }
+  // Items of bin b, in the (largest-first) order they were assigned.
+  std::vector<int32_t> count(nb + 1, 0);
+  for (size_t i = 0; i < n; ++i) ++count[bin_of[i] + 1];
+  for (int b = 0; b < nb; ++b) count[b + 1] += count[b];
+  bins->assign(count.begin(), count.end());
+  std::vector<WorkItem> out(n);
+  for (size_t i = 0; i < n; ++i) out[count[bin_of[i]]++] = (*items)[i];
   *items = std::move(out);
 }
 
@@ -256,8 +295,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   // stream into about one item per resident workgroup slot, no shard below
   // 256 keys, so every slot streams a similar number of bytes (ADR-0060,
   // §5.2-§5.3: decode is bound by KV loads).
-  const int64_t slots = 2LL * in.n_cu;                              // narrow: 2 workgroups per CU
-  const int64_t wide_slots = (in.dtype == 0 ? 1LL : 2LL) * in.n_cu;  // bf16 wide: one 8-wave workgroup per CU
+  const int64_t slots = 2LL * std::max(1, in.narrow_per_cu) * in.n_cu;   // about two items per resident workgroup
+  const int64_t wide_slots = (int64_t)std::max(1, in.wide_per_cu) * in.n_cu;
   {
     int64_t wn = 0;
     for (int32_t ui = 0; ui < nu; ++ui)
@@ -284,7 +323,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       // Cost units: one key of one item (the time a wave spends on one key
       // with 32 rows); fixed per-item cost ~ 96 keys; a partial row costs
       // its bytes at HBM speed relative to MFMA time per key.
-      const double item_fixed = 96.0;
+      const double item_fixed = kItemFixedKeys;
       const double merge_per_row = 0.002 * in.D / 128.0;
       double best = 1e300;
       int32_t best_chunk = maxlen;
@@ -377,7 +416,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   };
   std::stable_sort(P->wide.begin(), P->wide.end(), by_cost);
   std::stable_sort(P->narrow.begin(), P->narrow.end(), by_cost);
-  xcd_order(&P->wide, in.n_cu);
+  bin_items(&P->wide, in.wide_per_cu * in.n_cu, in.n_cu, &P->wide_bins);
+  bin_items(&P->narrow, in.narrow_per_cu * in.n_cu, in.n_cu, &P->narrow_bins);
 
   // Output rows that need the merge kernel (two or more live partials).
   for (int32_t b = 0; b < nb; ++b) {

@@ -22,14 +22,20 @@ struct PlanInput {
   std::vector<int32_t> b_group, b_qlen, b_priv;   // per branch
   std::vector<int32_t> splits_override;           // empty or n_groups + n_branches
   int32_t n_cu = 256;                             // compute units of the device
+  int32_t wide_per_cu = 1;                        // resident workgroups per CU, 128/256-row kernel
+  int32_t narrow_per_cu = 1;                      // resident workgroups per CU, 32-row kernel
 };
 
 struct Plan {
   std::vector<UnitDesc> units;
   std::vector<BranchDesc> branches;
   std::vector<TileInfo> tiles;
-  std::vector<WorkItem> wide;       // items for the 128-row kernel
-  std::vector<WorkItem> narrow;     // items for the 32-row kernel
+  std::vector<WorkItem> wide;       // items for the 128/256-row kernel, in bin order
+  std::vector<WorkItem> narrow;     // items for the 32-row kernel, in bin order
+  // Workgroup b of a kernel runs items [bins[b], bins[b+1]) in order; there
+  // are at most as many bins as workgroups stay resident on the device.
+  std::vector<int32_t> wide_bins;
+  std::vector<int32_t> narrow_bins;
   std::vector<int32_t> api_splits;  // per group prefix, then per branch suffix
   std::vector<int32_t> unit_slot;   // unit -> index in api_splits
   int64_t part_rows = 0;            // partial rows in the workspace

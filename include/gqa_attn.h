@@ -160,11 +160,14 @@ gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
                                  int64_t* n_forwards);
 
 /* Host-only planner check (no device use): plans the given metadata with
- * the handle-free parameters `p` and writes, for every work item, the tuple
- * (unit, kv_head, row_begin, n_rows, key_begin, key_end, split, kernel) into
- * `items` (host, int32, 8 per item) when `items` is not NULL and `cap`
- * allows. Returns the item count through *n_items and the per-unit split
- * counts through `splits` (host, n_groups + n_branches entries, may be NULL). */
+ * the handle-free parameters `p` for a 256-CU device with one resident
+ * workgroup per CU and writes, for every work item, the tuple
+ * (unit, kv_head, row_begin, n_rows, key_begin, key_end, split, kernel, bin)
+ * into `items` (host, int32, 9 per item) when `items` is not NULL and `cap`
+ * allows. Items are listed per kernel in launch order: workgroup `bin` of
+ * that kernel runs its items one after another, in the order listed.
+ * Returns the item count through *n_items and the per-unit split counts
+ * through `splits` (host, n_groups + n_branches entries, may be NULL). */
 gqa_status gqa_attn_plan_host(const gqa_attn_params* p,
                               int32_t n_groups, const int32_t* group_shared_start,
                               const int32_t* group_shared_len,

@@ -67,7 +67,7 @@ def _covered_pairs(w, items):
         first_tok.setdefault(b.group, qb[bi])
         first_tok[ng + bi] = qb[bi]
     got = []
-    for (slot, kv, r0, nr, k0, k1, split, kern) in items:
+    for (slot, kv, r0, nr, k0, k1, split, kern, _bin) in items:
         for r in range(r0, r0 + nr):
             tok = first_tok[slot] + r // G_
             g = r % G_
@@ -154,6 +154,52 @@ def test_heuristic_fills_the_device():
     assert 256 <= len(wide) <= 1024, len(wide)
     items, splits, _ = _plan(get_workload("mixed_32dec_64x4"))
     assert all(s >= 1 for s in splits[1:])
+
+
+def _item_cost(it):
+    return it[5] - it[4] + 96       # keys plus the planner's fixed per-item cost
+
+
+@pytest.mark.parametrize("name", ["fanout_8x20_32k", "decode_8k", "prefill_32k", "mixed_32dec_64x4"])
+def test_bins_pack_items_onto_resident_workgroups(name):
+    """Each kernel's items are dealt to at most 256 workgroups (one per CU);
+    a workgroup's items are contiguous and largest first; no workgroup's
+    load exceeds the list-scheduling bound (mean load + largest item) by
+    more than the 2% that the XCD placement may cost."""
+    items, _, _ = _plan(get_workload(name))
+    for kern in (0, 1):
+        its = [it for it in items if it[7] == kern]
+        if not its:
+            continue
+        bins = [it[8] for it in its]
+        assert bins == sorted(bins), "items of a workgroup are not contiguous"
+        n_bins = max(bins) + 1
+        assert n_bins <= 256 and n_bins <= len(its)
+        load = [0] * n_bins
+        for it in its:
+            load[it[8]] += _item_cost(it)
+        for a, b in zip(its, its[1:]):
+            if a[8] == b[8]:
+                assert _item_cost(a) >= _item_cost(b)
+        bound = sum(load) / n_bins + max(_item_cost(it) for it in its)
+        assert max(load) <= 1.02 * bound, (max(load), bound)
+
+
+def test_fanout_bins_balance_and_share_l2():
+    """Fan-out: 240 prefix items (6 shards x 5 M-tiles x 8 KV heads) and 64
+    suffix items fill exactly 256 workgroups, none holding two prefix items;
+    the M-tiles of one (KV head, shard) sit on one XCD (bin residue mod 8)."""
+    items, _, _ = _plan(get_workload("fanout_8x20_32k"))
+    wide = [it for it in items if it[7] == 0]
+    assert max(it[8] for it in wide) + 1 == 256
+    per_bin = {}
+    for it in wide:
+        per_bin.setdefault(it[8], []).append(it)
+    assert all(sum(1 for it in v if it[0] == 0) <= 1 for v in per_bin.values())
+    xcd = {}
+    for it in wide:
+        xcd.setdefault((it[0], it[1], it[6]), set()).add(it[8] % 8)
+    assert all(len(v) == 1 for v in xcd.values())
 
 
 BAD = [
