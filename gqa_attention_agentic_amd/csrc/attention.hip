@@ -138,8 +138,8 @@ struct KvSrc {
   bool paged;
 };
 
-template <typename T, int D>
-__device__ __forceinline__ KvSrc<T> kv_src(const AttnArgs& a, const UnitDesc& u, int kv) {
+template <typename T, int D, class U>
+__device__ __forceinline__ KvSrc<T> kv_src(const AttnArgs& a, const U& u, int kv) {
   KvSrc<T> s;
   s.paged = u.kind != kShared;
   s.ps = a.page_size;
@@ -446,21 +446,35 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, const Row& w, int kv, 
   s.l = 0.f;
 }
 
-// Final or partial write of one lane's row for O^T blocks [db0, db1).
-template <class C, typename T, int D>
-__device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it, const UnitDesc& u,
-                                          const Row& w, float m, float l, const f32x16_t* o,
-                                          int db0, int db1, bool write_scalars, int h) {
-  if (!w.ok) return;
+// Where one lane's row goes: the output row itself when the row has exactly
+// one live partial in total (written normalised, with its LSE), else this
+// item's slot in the partial workspace.
+struct RowDest {
+  bool direct;
+  int64_t row;   // direct: (token, head) index into o / lse; else the partial row
+};
+
+__device__ __forceinline__ RowDest row_dest(const AttnArgs& a, const WorkItem& it, const UnitDesc& u, const Row& w) {
+  RowDest d{false, 0};
+  if (!w.ok) return d;
   int64_t base_own, base_oth;
   const int live_own = unit_live(a, it.unit, w.tok, w.g, it.kv, &base_own);
   const BranchDesc br = a.branches[w.b];
   const int oth = (u.kind == kShared) ? br.unit_pr : br.unit_sh;
   const int live_oth = (oth >= 0) ? unit_live(a, oth, w.tok, w.g, it.kv, &base_oth) : 0;
-  (void)live_own;
-  if (live_own + live_oth == 1) {
+  d.direct = live_own + live_oth == 1;
+  d.row = d.direct ? (int64_t)w.tok * a.H_q + it.kv * a.G + w.g : base_own + (int64_t)it.split * u.bm;
+  return d;
+}
+
+// Final or partial write of one lane's row for O^T blocks [db0, db1).
+template <class C, typename T, int D>
+__device__ __forceinline__ void write_row_to(const AttnArgs& a, const RowDest& dst, bool ok, float m, float l,
+                                             const f32x16_t* o, int db0, int db1, bool write_scalars, int h) {
+  if (!ok) return;
+  if (dst.direct) {
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    const int64_t orow = ((int64_t)w.tok * a.H_q + it.kv * a.G + w.g) * D;
+    const int64_t orow = dst.row * D;
     for (int db = db0; db < db1; ++db) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -477,11 +491,9 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it,
         }
       }
     }
-    if (write_scalars && h == 0)
-      a.lse[(int64_t)w.tok * a.H_q + it.kv * a.G + w.g] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : kNegInf;
+    if (write_scalars && h == 0) a.lse[dst.row] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : kNegInf;
   } else {
-    const int64_t prow = base_own + (int64_t)it.split * u.bm;
-    float* po = a.part_o + prow * D;
+    float* po = a.part_o + dst.row * D;
     for (int db = db0; db < db1; ++db) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -490,8 +502,16 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it,
                                           o[db - db0][4 * q4 + 2], o[db - db0][4 * q4 + 3]);
       }
     }
-    if (write_scalars && h == 0) a.part_ml[prow] = make_float2(m, l);
+    if (write_scalars && h == 0) a.part_ml[dst.row] = make_float2(m, l);
   }
+}
+
+template <class C, typename T, int D>
+__device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it, const UnitDesc& u,
+                                          const Row& w, float m, float l, const f32x16_t* o,
+                                          int db0, int db1, bool write_scalars, int h) {
+  if (!w.ok) return;
+  write_row_to<C, T, D>(a, row_dest(a, it, u, w), true, m, l, o, db0, db1, write_scalars, h);
 }
 
 // Smallest / largest valid row position of the wave.
@@ -1001,15 +1021,18 @@ attn_narrow(AttnArgs a) {
 }
 
 // ---------------------------------------------------- narrow, bf16, DMA ----
-// KV-bandwidth-bound items (<= 32 rows, decode): each of the 4 waves streams
-// its own 32-key tiles (wave w takes tiles w, w+4, ...) through a private
-// 2-stage LDS ring filled by global->LDS DMA, with no barrier inside the
-// loop; for an item of up to 8 tiles every byte of its shard is requested at
-// kernel start. The four per-wave (m, l, O) states are merged through LDS at
-// the end. Same LDS swizzles, operand reads and softmax as the wide kernel.
+// KV-bandwidth-bound items (<= 32 rows, decode): each of the 8 waves streams
+// its own 32-key tiles (wave w takes tiles w, w+8, ...) through a private
+// LDS stage filled by global->LDS DMA, with no barrier inside the loop. An
+// item of up to 8 tiles (a 256-key shard) is requested in full at its start
+// and each wave then computes a single tile, so little compute is left once
+// the last bytes arrive. The eight per-wave (m, l, O) states are merged
+// through LDS at the end. Same LDS swizzles, operand reads and softmax as
+// the wide kernel.
 template <int D>
 struct NarrowDmaCfg {
   static constexpr bool BF16 = true;
+  static constexpr int WAVES = 8;
   static constexpr int BM = kNarrowRows;
   static constexpr int BN = 32;                     // keys per wave tile
   static constexpr int ROW = D * 2;
@@ -1017,16 +1040,17 @@ struct NarrowDmaCfg {
   static constexpr int NINST = TB / 1024;           // 1 KB DMA instructions per tensor per tile
   static constexpr int PER_WAVE = NINST;            // each wave issues its whole tile
   static constexpr int OB = D / 32, QF = D / 16, SB = BN / 32;
-  static constexpr int MERGE_O = 4 * OB * 16 * 64 * 4;   // bytes of the per-wave O^T exchange
-  static_assert(4 * 2 * TB >= MERGE_O, "stage-0 ring must hold the merge exchange");
+  static constexpr int MERGE_O = WAVES * OB * 16 * 64 * 4;   // bytes of the per-wave O^T exchange
+  static_assert(WAVES * 2 * TB >= MERGE_O, "the stages must hold the merge exchange");
+  static_assert(OB <= WAVES, "one wave per O^T block in the final combination");
 };
 
 template <int D>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(512, 2)
 attn_narrow_dma(AttnArgs a) {
   using C = NarrowDmaCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char st0[4 * 2 * C::TB];   // per wave: K tile then V tile
-  __shared__ __attribute__((aligned(1024))) char st1[4 * 2 * C::TB];
+  __shared__ __attribute__((aligned(1024))) char st[C::WAVES * 2 * C::TB];   // per wave: K tile then V tile
+  __shared__ float2 mml[C::WAVES * 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const DmaLane<C> L = dma_lane<C>(0, lane);
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
@@ -1035,84 +1059,78 @@ attn_narrow_dma(AttnArgs a) {
     // stages are refilled.
     if (idx > bin_begin) __syncthreads();
     const WorkItem it = a.items[idx];
-    const UnitDesc u = a.units[it.unit];
-    const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+    const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, it, it.kv);
     const int kb0 = it.key_begin, ke = it.key_end, causal = a.causal;
     const int nt = (ke - kb0 + C::BN - 1) / C::BN;
-    constexpr int VM = 2 * C::NINST;
-    char* K0 = st0 + wave * 2 * C::TB;
+    char* K0 = st + wave * 2 * C::TB;
     char* V0 = K0 + C::TB;
-    char* K1 = st1 + wave * 2 * C::TB;
-    char* V1 = K1 + C::TB;
-    // The first tiles' DMA goes out before the row bookkeeping and Q loads,
-    // whose dependent lookups would otherwise delay it.
-    if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
-    if (wave + 4 < nt) dma_tile_any<C, D>(src, L, 0, kb0 + (wave + 4) * C::BN, ke, K1, V1);
-    const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+    // Q first, then the K/V stream: both need only the work item, and Q
+    // issued behind a whole shard of K/V would arrive last. The unit and
+    // branch lookups (row positions) follow under the stream.
+    const int r = it.row_begin + i;
+    Row w;
+    w.ok = i < it.n_rows;
+    w.tok = it.tok_begin + r / a.G;
+    w.g = r - (r / a.G) * a.G;
     State<C> s;
     load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+    if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
+    const UnitDesc u = a.units[it.unit];
+    w = row_of(a, u, r, w.ok);
+    // The output lookups (unit, tile and branch records) are dependent
+    // loads: resolve them now, under the K/V stream, not after the merge.
+    const RowDest dst = row_dest(a, it, u, w);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
     const bool active = it.n_rows > 0;
     const float c = a.scale_log2;
-    for (int j = wave; j < nt; j += 8) {
-      if (j + 4 < nt) wait_dma<VM>();
-      else wait_dma<0>();
+    for (int j = wave; j < nt; j += C::WAVES) {
+      wait_dma<0>();
       dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, u, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
                      i, h);
-      if (j + 8 < nt) {
-        wait_dma<63>();   // own LDS reads of stage 0 done
-        dma_tile_any<C, D>(src, L, 0, kb0 + (j + 8) * C::BN, ke, K0, V0);
-      }
-      const int j2 = j + 4;
-      if (j2 >= nt) break;
-      if (j2 + 4 < nt) wait_dma<VM>();
-      else wait_dma<0>();
-      dma_step<C, D>(lds_u32(K1), lds_u32(V1), L, s, u, kb0 + j2 * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
-                     i, h);
-      if (j2 + 8 < nt) {
-        wait_dma<63>();
-        dma_tile_any<C, D>(src, L, 0, kb0 + (j2 + 8) * C::BN, ke, K1, V1);
+      if (j + C::WAVES < nt) {
+        wait_dma<63>();   // own LDS reads of the stage done
+        dma_tile_any<C, D>(src, L, 0, kb0 + (j + C::WAVES) * C::BN, ke, K0, V0);
       }
     }
-    // Merge the four waves' states (same rows, disjoint keys) through LDS.
+    // Merge the eight waves' states (same rows, disjoint keys) through LDS.
     s.l += __shfl_xor(s.l, 32);
     wait_dma<0>();
     __syncthreads();
-    float* mo = (float*)st0;                       // [wave][db][r][lane]
-    float2* mml = (float2*)st1;
+    float* mo = (float*)st;                       // [wave][db][r][lane]
 #pragma unroll
     for (int db = 0; db < C::OB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
     mml[wave * 64 + lane] = make_float2(s.m, s.l);
     __syncthreads();
-    float mk[4], lk[4];
-    float M = kNegInf;
+    if (wave < C::OB) {
+      float mk[C::WAVES], lk[C::WAVES];
+      float M = kNegInf;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float2 x = mml[k * 64 + lane];
-      mk[k] = x.x;
-      lk[k] = x.y;
-      M = fmaxf(M, x.x);
-    }
-    const float M_use = (M == kNegInf) ? 0.f : M;
-    float Lsum = 0.f, wk[4];
+      for (int k = 0; k < C::WAVES; ++k) {
+        const float2 x = mml[k * 64 + lane];
+        mk[k] = x.x;
+        lk[k] = x.y;
+        M = fmaxf(M, x.x);
+      }
+      const float M_use = (M == kNegInf) ? 0.f : M;
+      float Lsum = 0.f, wk[C::WAVES];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      wk[k] = exp2_fast(mk[k] - M_use);
-      Lsum += lk[k] * wk[k];
-    }
-    for (int db = wave; db < C::OB; db += 4) {
+      for (int k = 0; k < C::WAVES; ++k) {
+        wk[k] = exp2_fast(mk[k] - M_use);
+        Lsum += lk[k] * wk[k];
+      }
+      const int db = wave;
       f32x16_t acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float x = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
+        for (int k = 0; k < C::WAVES; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
         acc[r] = x;
       }
-      write_row<C, uint16_t, D>(a, it, u, w, M, Lsum, &acc, db, db + 1, wave == 0, h);
+      write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
     }
   }
 }
@@ -1198,7 +1216,7 @@ hipError_t launch_attn_t(const AttnArgs& a, int32_t n_bins, bool narrow, hipStre
                          hipEvent_t e1) {
   if (n_bins <= 0) return hipSuccess;
   if (narrow) {
-    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_bins, 256);
+    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_bins, 512);
     else GQA_LAUNCH((attn_narrow<T, D>), n_bins, 256);
   } else if constexpr (std::is_same<T, uint16_t>::value) {
     GQA_LAUNCH((attn_wide_dma<D>), n_bins, 512);
@@ -1214,7 +1232,7 @@ hipError_t occupancy_t(bool narrow, int* per_cu) {
   hipError_t e;
   if (narrow) {
     if constexpr (std::is_same<T, uint16_t>::value)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow_dma<D>, 256, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow_dma<D>, 512, 0);
     else
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow<T, D>, 256, 0);
   } else if constexpr (std::is_same<T, uint16_t>::value) {

@@ -397,6 +397,10 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           w.key_end = std::min(bnd[s + 1], kend);
           w.split = s;
           w.tile = (int32_t)t;
+          w.kind = u.kind;
+          w.src = u.src;
+          w.tok_begin = u.tok_begin;
+          w.pad = 0;
           P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
           (u.bm != kNarrowRows ? P->wide : P->narrow).push_back(w);
         }

@@ -69,6 +69,12 @@ struct WorkItem {
   int32_t key_end;
   int32_t split;       // shard index (partial slot)
   int32_t tile;        // M-tile index within the unit
+  // Copies of the unit's kind, src and tok_begin, so that the Q loads and
+  // the K/V stream can be issued before the unit record arrives.
+  int32_t kind;
+  int32_t src;
+  int32_t tok_begin;
+  int32_t pad;
 };
 
 }  // namespace gqa
