@@ -59,9 +59,11 @@ struct gqa_attn {
   size_t h_staging_cap = 0;
   hipEvent_t staging_free = nullptr;   // recorded after the last staging -> device copy
   size_t off_wide = 0, off_narrow = 0, off_wide_bins = 0, off_narrow_bins = 0, off_units = 0, off_branches = 0,
-         off_tiles = 0;
-  // partial workspace
+         off_tiles = 0, off_tok_need = 0;
+  // workspace: arrival counters (one per query token and KV head), then the
+  // partial (m, l) and O rows
   char* d_work = nullptr;
+  bool counters_dirty = true;   // counters must be cleared before the next launch
   size_t d_work_cap = 0;
   // timing
   bool timing = false;
@@ -145,6 +147,8 @@ size_t plan_layout(gqa_attn* h) {
   off = align_up(off + P.branches.size() * sizeof(gqa::BranchDesc), 256);
   h->off_tiles = off;
   off = align_up(off + P.tiles.size() * sizeof(gqa::TileInfo), 256);
+  h->off_tok_need = off;
+  off = align_up(off + P.tok_need.size() * sizeof(int32_t), 256);
   return std::max<size_t>(off, 256);
 }
 
@@ -186,6 +190,7 @@ gqa_status upload_plan(gqa_attn* h, hipStream_t stream) {
   put(h->off_units, P.units.data(), P.units.size() * sizeof(gqa::UnitDesc));
   put(h->off_branches, P.branches.data(), P.branches.size() * sizeof(gqa::BranchDesc));
   put(h->off_tiles, P.tiles.data(), P.tiles.size() * sizeof(gqa::TileInfo));
+  put(h->off_tok_need, P.tok_need.data(), P.tok_need.size() * sizeof(int32_t));
   e = hipMemcpyAsync(h->d_plan, h->h_staging, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
   if (!h->staging_free) {
@@ -197,9 +202,16 @@ gqa_status upload_plan(gqa_attn* h, hipStream_t stream) {
   return GQA_OK;
 }
 
+// Bytes of the arrival counters at the start of the workspace.
+size_t counter_bytes(const gqa_attn* h) {
+  return h->plan.part_rows ? align_up((size_t)h->plan.n_q_tokens * h->p.num_kv_heads * sizeof(int32_t), 256) : 0;
+}
+
 gqa_status ensure_workspace(gqa_attn* h) {
   const size_t rows = (size_t)h->plan.part_rows;
-  const size_t need = rows ? align_up(rows * sizeof(float2), 256) + rows * (size_t)h->p.head_dim * sizeof(float) : 0;
+  const size_t need = rows ? counter_bytes(h) + align_up(rows * sizeof(float2), 256) +
+                                 rows * (size_t)h->p.head_dim * sizeof(float)
+                           : 0;
   if (h->p.workspace_bytes_cap > 0 && need > (size_t)h->p.workspace_bytes_cap)
     return fail(GQA_ERR_NO_MEMORY, "partial workspace of " + std::to_string(need) +
                                        " bytes exceeds workspace_bytes_cap");
@@ -214,6 +226,7 @@ gqa_status ensure_workspace(gqa_attn* h) {
   e = hipMalloc((void**)&h->d_work, need);
   if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "workspace allocation of " + std::to_string(need) + " bytes failed");
   h->d_work_cap = need;
+  h->counters_dirty = true;
   return GQA_OK;
 }
 
@@ -336,6 +349,7 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
     h->plan = std::move(fresh);
     h->key = std::move(key);
     h->have_plan = true;
+    h->counters_dirty = true;   // the counter layout follows the plan
     s = upload_plan(h, st);
     if (s != GQA_OK) {
       h->have_plan = false;
@@ -344,6 +358,14 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   }
   s = ensure_workspace(h);
   if (s != GQA_OK) return s;
+  // Every forward leaves the counters at zero (the item that completes a
+  // token resets its counter); they are cleared here only after the plan or
+  // the workspace changed.
+  if (h->counters_dirty && counter_bytes(h) > 0) {
+    e = hipMemsetAsync(h->d_work, 0, counter_bytes(h), st);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(counters)");
+    h->counters_dirty = false;
+  }
 
   const gqa::Plan& Q = h->plan;
   gqa::AttnArgs a{};
@@ -356,8 +378,10 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   a.units = (const gqa::UnitDesc*)(h->d_plan + h->off_units);
   a.branches = (const gqa::BranchDesc*)(h->d_plan + h->off_branches);
   a.tiles = (const gqa::TileInfo*)(h->d_plan + h->off_tiles);
-  a.part_ml = (float2*)h->d_work;
-  a.part_o = (float*)(h->d_work + align_up((size_t)Q.part_rows * sizeof(float2), 256));
+  a.tok_need = (const int32_t*)(h->d_plan + h->off_tok_need);
+  a.counters = (int32_t*)h->d_work;
+  a.part_ml = (float2*)(h->d_work + counter_bytes(h));
+  a.part_o = (float*)(h->d_work + counter_bytes(h) + align_up((size_t)Q.part_rows * sizeof(float2), 256));
   a.o = o;
   a.lse = lse;
   a.max_pages = max_pages_per_branch;
@@ -379,7 +403,7 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   if (tm) {
     tm->wide = !Q.wide.empty();
     tm->narrow = !Q.narrow.empty();
-    tm->merged = Q.merge_rows > 0;
+    tm->merged = Q.merge_launch;
   }
   if (!Q.wide.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
@@ -395,7 +419,7 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
                               ev(3));
     if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
   }
-  if (Q.merge_rows > 0) {
+  if (Q.merge_launch) {
     e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, Q.max_row_parts, st, ev(4), ev(5));
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }

@@ -514,6 +514,126 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it,
   write_row_to<C, T, D>(a, row_dest(a, it, u, w), true, m, l, o, db0, db1, write_scalars, h);
 }
 
+// ------------------------------------------------------- combination ----
+// Log-sum-exp combination of the split-KV partials of output row (tok, kv,
+// g), d values d0 .. d0 + 3 (ADR-0060 GQA fused attention, §4: m = max m_i,
+// weights 2^(m_i - m), one normalisation at the end). Partials are folded in
+// a fixed order -- prefix shards, then suffix shards -- with the same online
+// rule as the tile loop, so the result does not depend on which item does
+// it. Rows with a single partial were written by their item directly.
+template <typename T, int D, int U>
+__device__ __forceinline__ void combine_row(const AttnArgs& a, int tok, int kv, int g, int d0) {
+  // U: partial loads in flight per fold step (the partials come from other
+  // XCDs, so each step costs a full memory round trip)
+  const int b = branch_of(a.branches, 0, a.n_branches, tok);
+  const BranchDesc br = a.branches[b];
+  int64_t base[2] = {0, 0};
+  int live[2] = {0, 0}, bm[2] = {0, 0};
+  if (br.unit_sh >= 0) {
+    live[0] = unit_live(a, br.unit_sh, tok, g, kv, &base[0]);
+    bm[0] = a.units[br.unit_sh].bm;
+  }
+  if (br.unit_pr >= 0) {
+    live[1] = unit_live(a, br.unit_pr, tok, g, kv, &base[1]);
+    bm[1] = a.units[br.unit_pr].bm;
+  }
+  const int n = live[0] + live[1];
+  if (n < 2) return;
+  float M = kNegInf, L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q0 = 0; q0 < n; q0 += U) {
+    float2 ml[U];
+    float4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int q = q0 + k;
+      if (q < n) {
+        const int64_t p = (q < live[0]) ? base[0] + (int64_t)q * bm[0] : base[1] + (int64_t)(q - live[0]) * bm[1];
+        ml[k] = a.part_ml[p];
+        v[k] = *(const float4*)(a.part_o + p * D + d0);
+      } else {
+        ml[k] = make_float2(kNegInf, 0.f);
+        v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const float Mn = fmaxf(M, ml[k].x);
+      const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+      const float sa = exp2_fast(M - Mu), sb = exp2_fast(ml[k].x - Mu);
+      L = L * sa + ml[k].y * sb;
+      O.x = O.x * sa + v[k].x * sb;
+      O.y = O.y * sa + v[k].y * sb;
+      O.z = O.z * sa + v[k].z * sb;
+      O.w = O.w * sa + v[k].w * sb;
+      M = Mn;
+    }
+  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  const int64_t orow = ((int64_t)tok * a.H_q + kv * a.G + g);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    uint2 pk;
+    pk.x = pack_bf16x2(O.x * inv, O.y * inv);
+    pk.y = pack_bf16x2(O.z * inv, O.w * inv);
+    *(uint2*)((uint16_t*)a.o + orow * D + d0) = pk;
+  } else {
+    *(float4*)((float*)a.o + orow * D + d0) = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+  }
+  if (d0 == 0) a.lse[orow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+}
+
+// Called by every thread of a narrow-kernel workgroup once its item's rows
+// are written. Tokens whose partials all come from narrow items (decode-like
+// rows: a few rows over a long KV range cut into many shards) are combined
+// here, which spares them the separate merge launch; the MFMA-bound items
+// leave theirs to lse_merge, since a combining workgroup would stall its
+// CU. Each such token has a counter per KV head; the item that
+// brings it to the planned number of arrivals combines the token's rows.
+// Release before the increment and acquire after the winning one (device
+// scope: the XCDs' L2 caches are not coherent with each other) make every
+// other item's partials visible. The winner resets the counter, so all
+// counters are zero again when the launch ends. Work per workgroup is
+// bounded and no thread waits on another workgroup.
+// The item is read again here (through an opaque copy of its index) rather
+// than kept live across the tile loop, where its registers are needed.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void combine_if_last(const AttnArgs& a, int idx, int tid, int* won) {
+  int ix = idx;
+  asm volatile("" : "+v"(ix));
+  const WorkItem it = a.items[ix];
+  if (it.n_rows <= 0) return;
+  const int32_t* tok_need = a.tok_need;
+  int32_t* counters = a.counters;
+  const int tok0 = it.tok_begin + it.row_begin / a.G;
+  const int ntok = it.tok_begin + (it.row_begin + it.n_rows - 1) / a.G - tok0 + 1;
+  __syncthreads();   // this workgroup's partial stores are complete
+  int mine = 0;
+  for (int k = tid; k < ntok; k += NT) {
+    const int tok = tok0 + k;
+    const int need = tok_need[tok];
+    int w = 0;
+    if (need > 0) {
+      int* c = counters + (int64_t)tok * a.H_kv + it.kv;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (atomicAdd(c, 1) == need - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        atomicExch(c, 0);
+        w = 1;
+      }
+    }
+    won[k] = w;
+    mine |= w;
+  }
+  if (!__syncthreads_or(mine)) return;
+  const int per_tok = a.G * (D / 4);
+  for (int x = tid; x < ntok * per_tok; x += NT) {
+    const int k = x / per_tok;
+    if (!won[k]) continue;
+    const int rem = x - k * per_tok;
+    combine_row<T, D, 16>(a, tok0 + k, it.kv, rem / (D / 4), (rem % (D / 4)) * 4);
+  }
+}
+
 // Smallest / largest valid row position of the wave.
 __device__ __forceinline__ void wave_pos_range(const Row& w, int* pmin, int* pmax) {
   int lo = w.ok ? w.pos : 0x7fffffff, hi = w.ok ? w.pos : -1;
@@ -945,6 +1065,7 @@ __global__ void __launch_bounds__(256, (Cfg<T, D, true>::WAVES_PER_SIMD))
 attn_narrow(AttnArgs a) {
   using C = Cfg<T, D, true>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ int won[C::BM];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
   for (int idx = bin_begin; idx < bin_end; ++idx) {
@@ -1017,6 +1138,7 @@ attn_narrow(AttnArgs a) {
       }
       write_row<C, T, D>(a, it, u, w, M, L, &acc, db, db + 1, wave == 0, h);
     }
+    combine_if_last<T, D, 256>(a, idx, tid, won);
   }
 }
 
@@ -1051,6 +1173,7 @@ attn_narrow_dma(AttnArgs a) {
   using C = NarrowDmaCfg<D>;
   __shared__ __attribute__((aligned(1024))) char st[C::WAVES * 2 * C::TB];   // per wave: K tile then V tile
   __shared__ float2 mml[C::WAVES * 64];
+  __shared__ int won[C::BM];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const DmaLane<C> L = dma_lane<C>(0, lane);
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
@@ -1132,12 +1255,14 @@ attn_narrow_dma(AttnArgs a) {
       }
       write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
     }
+    combine_if_last<uint16_t, D, 512>(a, idx, tid, won);
   }
 }
 
 // --------------------------------------------------------------- merge ----
 // One workgroup per (query token, KV head); each thread owns 4 consecutive
-// d values of one of the G rows. Partials are folded in a fixed order
+// d values of one of the G rows. Tokens whose partials all come from the
+// narrow kernel were combined there (combine_if_last) and are skipped. Partials are folded in a fixed order
 // (prefix shards, then suffix shards) with the same online rule as the
 // tile loop, so the result is bitwise repeatable (ADR-0060 GQA fused
 // attention, §4: m = max m_i, weights exp(m_i - m), normalise once at the
@@ -1146,6 +1271,7 @@ template <typename T, int D, int U>
 __global__ void __launch_bounds__(256)
 lse_merge(AttnArgs a) {
   const int tok = blockIdx.x / a.H_kv, kv = blockIdx.x - tok * a.H_kv;
+  if (a.tok_need[tok] > 0) return;
   constexpr int TPR = D / 4;   // threads per row
   const int b = branch_of(a.branches, 0, a.n_branches, tok);
   const BranchDesc br = a.branches[b];
@@ -1275,6 +1401,7 @@ hipError_t attention_occupancy(int dtype, int head_dim, bool narrow, int* per_cu
                                          : occupancy_t<uint16_t, 64>(narrow, per_cu);
   return head_dim == 128 ? occupancy_t<float, 128>(narrow, per_cu) : occupancy_t<float, 64>(narrow, per_cu);
 }
+
 
 hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream,
                         hipEvent_t ev_start, hipEvent_t ev_stop) {

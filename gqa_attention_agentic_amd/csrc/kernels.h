@@ -19,6 +19,8 @@ struct AttnArgs {
   const UnitDesc* units;
   const BranchDesc* branches;
   const TileInfo* tiles;
+  const int32_t* tok_need;  // per query token: narrow items whose arrival completes it (0: not combined in-launch)
+  int32_t* counters;        // [n_q_tokens, H_kv] arrival counters, zero between launches
   float* part_o;        // [part_rows, D] unnormalised partial O
   float2* part_ml;      // [part_rows] (m in log2 units, l)
   void* o;              // [n_q_tokens, H_q, D] storage dtype
@@ -49,9 +51,11 @@ hipError_t launch_attention(const AttnArgs& a, int32_t n_bins, bool narrow, int 
 // resident on one CU at once (at least 1).
 hipError_t attention_occupancy(int dtype, int head_dim, bool narrow, int* per_cu);
 
-// Log-sum-exp merge of the partials of every output row with >= 2 of them.
-// max_parts: the largest number of partials any output row has.
+// Log-sum-exp merge of the partials of every output row with >= 2 of them
+// that was not combined inside the narrow kernel. max_parts: the largest
+// number of partials any output row has.
 hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_parts, hipStream_t stream,
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
 
 }  // namespace gqa

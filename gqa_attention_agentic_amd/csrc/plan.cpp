@@ -423,11 +423,17 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   bin_items(&P->wide, in.wide_per_cu * in.n_cu, in.n_cu, &P->wide_bins);
   bin_items(&P->narrow, in.narrow_per_cu * in.n_cu, in.n_cu, &P->narrow_bins);
 
-  // Output rows that need the merge kernel (two or more live partials).
+  // Output rows that need combining (two or more live partials). A token
+  // whose partials all come from narrow items is combined by the last of
+  // them to finish: tok_need counts those of every M-tile that holds one of
+  // the token's G rows, in both of its units. Any other token with such rows
+  // goes to the merge kernel.
+  P->tok_need.assign(P->n_q_tokens, 0);
   for (int32_t b = 0; b < nb; ++b) {
     const BranchDesc& br = P->branches[b];
     for (int32_t t = 0; t < br.q_len; ++t) {
       const int32_t tok = br.q_begin + t;
+      bool any = false;
       for (int32_t g = 0; g < G; ++g) {
         int32_t n = 0;
         for (int32_t ui : {br.unit_sh, br.unit_pr}) {
@@ -436,9 +442,27 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           const int64_t r = (int64_t)(tok - u.tok_begin) * G + g;
           n += P->tiles[u.tile_off + r / u.bm].live;
         }
-        if (n >= 2) P->merge_rows += in.H_kv;
+        if (n >= 2) {
+          P->merge_rows += in.H_kv;
+          any = true;
+        }
         P->max_row_parts = std::max(P->max_row_parts, n);
       }
+      if (!any) continue;
+      int32_t items = 0;
+      bool narrow_only = true;
+      for (int32_t ui : {br.unit_sh, br.unit_pr}) {
+        if (ui < 0) continue;
+        const UnitDesc& u = P->units[ui];
+        const int64_t r0 = (int64_t)(tok - u.tok_begin) * G, r1 = r0 + G - 1;
+        for (int64_t tl = r0 / u.bm; tl <= r1 / u.bm; ++tl) {
+          const int32_t live = P->tiles[u.tile_off + tl].live;
+          items += live;
+          if (live > 0 && u.bm != kNarrowRows) narrow_only = false;
+        }
+      }
+      if (narrow_only) P->tok_need[tok] = items;
+      else P->merge_launch = true;
     }
   }
   return "";

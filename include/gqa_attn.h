@@ -24,7 +24,9 @@
  * tokens of all branches of a group into one M dimension (ADR-0060, §5.2;
  * AHBM Agentic Runtime Architecture, §3.2), splits each KV range into shards
  * whose (m, l, O) partials are combined by a log-sum-exp merge (ADR-0060,
- * §4), and skips KV tiles that lie entirely in the future of a query block
+ * §4: in a separate merge launch, or, for rows whose partials all come from
+ * the decode-like kernel, by the last of their items to finish), and skips
+ * KV tiles that lie entirely in the future of a query block
  * (ADR-0060, §5.4). None of that is visible in the result beyond rounding.
  *
  * Conventions
@@ -153,8 +155,11 @@ gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n);
  * stop events). enable != 0 starts recording (and clears earlier records).
  * gqa_attn_kernel_times waits for the recorded events and returns the summed
  * milliseconds of every forward since timing was enabled -- attn_ms sums the
- * attention launches (wide and narrow), merge_ms the merge launch -- and the
- * number of forwards, then clears the records. */
+ * attention launches (wide and narrow), merge_ms the separate merge launch --
+ * and the number of forwards, then clears the records. Rows whose partials
+ * all come from the narrow (decode-like) kernel are combined inside that
+ * launch, so their merge time is part of attn_ms; a forward with no other
+ * such rows makes no merge launch and adds 0 to merge_ms. */
 gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable);
 gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
                                  int64_t* n_forwards);

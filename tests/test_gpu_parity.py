@@ -141,6 +141,30 @@ def test_determinism_bitwise():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_alternating_plans_on_one_handle():
+    """One handle alternating between two plans (fan-out with a split prefix,
+    then a 6-shard decode) four times: the per-token arrival counters of the
+    in-launch combination must be back at zero after every forward, and be
+    cleared when the layout changes, so every result matches the oracle and
+    repeats bit for bit."""
+    wa = custom("alt_fanout", H_q=16, H_kv=2, d=128, page_size=16, shared=(900,),
+                branches=((0, 5, 37), (0, 7, 50), (0, 3, 9)), seed=121, splits=[4, 1, 1, 1])
+    wb = custom("alt_decode", H_q=16, H_kv=2, d=128, shared=(1500,), branches=((0, 1, 0),), causal=False,
+                seed=122, splits=[6, 0])
+    ia, ib = generate(wa, "cuda"), generate(wb, "cuda")
+    ra, rb = H.oracle_rows(wa, ia), H.oracle_rows(wb, ib)
+    h = H.handle_for(wa)
+    first = {}
+    for rep in range(4):
+        for w, inp, ref in ((wa, ia, ra), (wb, ib, rb)):
+            o, lse, _ = H.run_library(w, inp, handle=h)
+            H.compare(w, o, lse, ref[0], ref[1], ref[2], label=f"{w.name} #{rep}")
+            if w.name in first:
+                assert torch.equal(o, first[w.name][0]) and torch.equal(lse, first[w.name][1]), w.name
+            else:
+                first[w.name] = (o.clone(), lse.clone())
+
+
 def test_causal_future_keys_ignored():
     """Garbage (NaN) in keys after every query position never reaches O."""
     w = custom("future", shared=(200,), branches=((0, 64, 0),), seed=118)
