@@ -125,7 +125,7 @@ void fill_stats(const gqa::Plan& P, int64_t D, gqa_plan_stats* s) {
   s->workspace_bytes = P.part_rows * (D + 2) * (int64_t)sizeof(float);
   s->n_units = (int64_t)P.units.size();
   s->max_splits = P.max_splits;
-  s->reserved = 0;
+  s->merge_launch = P.merge_launch ? 1 : 0;
 }
 
 // Serialised plan: wide items | narrow items | wide bins | narrow bins |

@@ -141,7 +141,9 @@ typedef struct {
   int64_t workspace_bytes;    /* partial-state workspace in use                   */
   int64_t n_units;            /* group prefixes + branch suffixes with keys       */
   int32_t max_splits;         /* largest split count of any unit                  */
-  int32_t reserved;
+  int32_t merge_launch;       /* 1 if the forward makes a separate merge launch;
+                                 0 when every row with several partials is
+                                 combined inside the narrow attention launch */
 } gqa_plan_stats;
 gqa_status gqa_attn_plan_stats(const gqa_attn* h, gqa_plan_stats* out);
 

@@ -202,6 +202,17 @@ def test_fanout_bins_balance_and_share_l2():
     assert all(len(v) == 1 for v in xcd.values())
 
 
+@pytest.mark.parametrize("name,launch", [("decode_8k", 0), ("fanout_8x20_32k", 1), ("prefill_32k", 1),
+                                         ("mixed_32dec_64x4", 1)])
+def test_merge_launch_only_when_wide_partials(name, launch):
+    """Rows whose partials all come from the narrow kernel are combined inside
+    it: a decode forward has no separate merge launch; workloads with rows
+    split over the MFMA kernel keep it."""
+    _, _, stats = _plan(get_workload(name))
+    assert stats["n_merge_rows"] > 0
+    assert stats["merge_launch"] == launch
+
+
 BAD = [
     (dict(H_q=6, H_kv=4), "multiple"),
     (dict(d=96), "head_dim"),
