@@ -58,8 +58,7 @@ struct gqa_attn {
   char* h_staging = nullptr;
   size_t h_staging_cap = 0;
   hipEvent_t staging_free = nullptr;   // recorded after the last staging -> device copy
-  size_t off_wide = 0, off_narrow = 0, off_wide_bins = 0, off_narrow_bins = 0, off_units = 0, off_branches = 0,
-         off_tiles = 0, off_tok_need = 0;
+  size_t off_wide = 0, off_narrow = 0, off_wide_bins = 0, off_narrow_bins = 0, off_tok_rec = 0, off_combs = 0;
   // workspace: arrival counters (one per query token and KV head), then the
   // partial (m, l) and O rows
   char* d_work = nullptr;
@@ -84,6 +83,10 @@ gqa_status check_params(const gqa_attn_params* p) {
   if (p->page_size <= 0 || p->page_size > 4096)
     return fail(GQA_ERR_INVALID_ARG, "page_size must be in 1..4096");
   if (p->dtype != GQA_BF16 && p->dtype != GQA_FP32) return fail(GQA_ERR_INVALID_ARG, "unknown dtype");
+  // An M-tile holds whole tokens: the G query heads of a KV head must fit one.
+  const int max_g = (p->dtype == GQA_BF16) ? gqa::kWideRowsBf16 : gqa::kWideRows;
+  if (p->num_q_heads / p->num_kv_heads > max_g)
+    return fail(GQA_ERR_UNSUPPORTED, "more than " + std::to_string(max_g) + " query heads per KV head");
   if (p->workspace_bytes_cap < 0) return fail(GQA_ERR_INVALID_ARG, "workspace_bytes_cap < 0");
   if (!(std::isfinite(p->softmax_scale))) return fail(GQA_ERR_INVALID_ARG, "softmax_scale is not finite");
   return GQA_OK;
@@ -129,7 +132,7 @@ void fill_stats(const gqa::Plan& P, int64_t D, gqa_plan_stats* s) {
 }
 
 // Serialised plan: wide items | narrow items | wide bins | narrow bins |
-// units | branches | tiles.
+// token records | combination records.
 size_t plan_layout(gqa_attn* h) {
   const gqa::Plan& P = h->plan;
   size_t off = 0;
@@ -141,14 +144,10 @@ size_t plan_layout(gqa_attn* h) {
   off = align_up(off + P.wide_bins.size() * sizeof(int32_t), 256);
   h->off_narrow_bins = off;
   off = align_up(off + P.narrow_bins.size() * sizeof(int32_t), 256);
-  h->off_units = off;
-  off = align_up(off + P.units.size() * sizeof(gqa::UnitDesc), 256);
-  h->off_branches = off;
-  off = align_up(off + P.branches.size() * sizeof(gqa::BranchDesc), 256);
-  h->off_tiles = off;
-  off = align_up(off + P.tiles.size() * sizeof(gqa::TileInfo), 256);
-  h->off_tok_need = off;
-  off = align_up(off + P.tok_need.size() * sizeof(int32_t), 256);
+  h->off_tok_rec = off;
+  off = align_up(off + P.tok_rec.size() * sizeof(gqa::TokRec), 256);
+  h->off_combs = off;
+  off = align_up(off + P.combs.size() * sizeof(gqa::CombTok), 256);
   return std::max<size_t>(off, 256);
 }
 
@@ -187,10 +186,8 @@ gqa_status upload_plan(gqa_attn* h, hipStream_t stream) {
   put(h->off_narrow, P.narrow.data(), P.narrow.size() * sizeof(gqa::WorkItem));
   put(h->off_wide_bins, P.wide_bins.data(), P.wide_bins.size() * sizeof(int32_t));
   put(h->off_narrow_bins, P.narrow_bins.data(), P.narrow_bins.size() * sizeof(int32_t));
-  put(h->off_units, P.units.data(), P.units.size() * sizeof(gqa::UnitDesc));
-  put(h->off_branches, P.branches.data(), P.branches.size() * sizeof(gqa::BranchDesc));
-  put(h->off_tiles, P.tiles.data(), P.tiles.size() * sizeof(gqa::TileInfo));
-  put(h->off_tok_need, P.tok_need.data(), P.tok_need.size() * sizeof(int32_t));
+  put(h->off_tok_rec, P.tok_rec.data(), P.tok_rec.size() * sizeof(gqa::TokRec));
+  put(h->off_combs, P.combs.data(), P.combs.size() * sizeof(gqa::CombTok));
   e = hipMemcpyAsync(h->d_plan, h->h_staging, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
   if (!h->staging_free) {
@@ -375,17 +372,14 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   a.k_pages = k_pages;
   a.v_pages = v_pages;
   a.page_table = page_table;
-  a.units = (const gqa::UnitDesc*)(h->d_plan + h->off_units);
-  a.branches = (const gqa::BranchDesc*)(h->d_plan + h->off_branches);
-  a.tiles = (const gqa::TileInfo*)(h->d_plan + h->off_tiles);
-  a.tok_need = (const int32_t*)(h->d_plan + h->off_tok_need);
+  a.tok_rec = (const gqa::TokRec*)(h->d_plan + h->off_tok_rec);
+  a.combs = (const gqa::CombTok*)(h->d_plan + h->off_combs);
   a.counters = (int32_t*)h->d_work;
   a.part_ml = (float2*)(h->d_work + counter_bytes(h));
   a.part_o = (float*)(h->d_work + counter_bytes(h) + align_up((size_t)Q.part_rows * sizeof(float2), 256));
   a.o = o;
   a.lse = lse;
   a.max_pages = max_pages_per_branch;
-  a.n_branches = n_branches;
   a.H_q = h->p.num_q_heads;
   a.H_kv = h->p.num_kv_heads;
   a.G = a.H_q / a.H_kv;

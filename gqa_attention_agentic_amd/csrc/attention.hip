@@ -61,29 +61,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Branch that owns query token `tok`: the last branch in [lo, hi) whose
-// first token is <= tok (branches with no tokens share their successor's
-// q_begin and are never returned for a real token).
-__device__ __forceinline__ int branch_of(const BranchDesc* br, int lo, int hi, int tok) {
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (br[mid].q_begin <= tok) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// Live partial count of unit `ui` for row (tok, g) and the workspace row of
-// its shard 0 for KV head kv (shard s is at base + s * bm).
-__device__ __forceinline__ int unit_live(const AttnArgs& a, int ui, int tok, int g, int kv,
-                                         int64_t* base) {
-  const UnitDesc& u = a.units[ui];
-  const int r = (tok - u.tok_begin) * a.G + g;
-  const int t = r / u.bm;
-  const TileInfo ti = a.tiles[u.tile_off + t];
-  *base = ti.part_off + ((int64_t)kv * ti.live) * u.bm + (r - t * u.bm);
-  return ti.live;
-}
-
 template <typename T, int D, bool NARROW>
 struct Cfg {
   static constexpr bool BF16 = std::is_same<T, uint16_t>::value;
@@ -395,33 +372,38 @@ __device__ __forceinline__ void compute_tile(const T* Ks, const T* Vs, State<C>&
 // diagonal or the ragged end of the shard (ADR-0060, §5.4: all-past tiles
 // carry no mask; all-future tiles were skipped by the caller).
 template <class C, typename T, int D>
-__device__ __forceinline__ void run_tile(const T* Ks, const T* Vs, State<C>& s, const UnitDesc& u,
+__device__ __forceinline__ void run_tile(const T* Ks, const T* Vs, State<C>& s, int key_pos0,
                                          int tk0, int key_end, int causal, int row_pos, int pmin,
                                          float c, int i, int h) {
   const int nvalid = min(C::BN, key_end - tk0);
-  const int kpos0 = u.key_pos0 + tk0;
+  const int kpos0 = key_pos0 + tk0;
   const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
   if (need_mask) compute_tile<C, T, D, true>(Ks, Vs, s, kpos0, nvalid, causal, row_pos, c, i, h);
   else compute_tile<C, T, D, false>(Ks, Vs, s, kpos0, nvalid, causal, row_pos, c, i, h);
 }
 
-// Per-lane row bookkeeping.
+// Per-lane row bookkeeping: row rloc of the item, i.e. the (token, g)
+// pair number row_begin + rloc of its unit. The token record gives the
+// position (for the causal mask) and whether the row's only partial is the
+// result. One load, with no dependence on any other record.
 struct Row {
-  int tok, g, b, pos;
-  bool ok;
+  int tok, g, pos;
+  bool ok;       // a valid row of the item
+  bool direct;   // exactly one live partial: O / l and the LSE are written directly
 };
 
-__device__ __forceinline__ Row row_of(const AttnArgs& a, const UnitDesc& u, int r, bool ok) {
+__device__ __forceinline__ Row row_at(const AttnArgs& a, const WorkItem& it, int rloc) {
   Row w;
-  w.ok = ok;
-  w.tok = u.tok_begin + r / a.G;
+  w.ok = rloc < it.n_rows;
+  const int r = it.row_begin + rloc;
+  w.tok = it.tok_begin + r / a.G;
   w.g = r - (r / a.G) * a.G;
-  w.b = u.branch_lo;
   w.pos = -1;
-  if (ok) {
-    w.b = (u.kind == kShared) ? branch_of(a.branches, u.branch_lo, u.branch_hi, w.tok) : u.src;
-    const BranchDesc br = a.branches[w.b];
-    w.pos = br.ctx_len - br.q_len + (w.tok - br.q_begin);
+  w.direct = false;
+  if (w.ok) {
+    const TokRec tr = a.tok_rec[w.tok];
+    w.pos = tr.pos;
+    w.direct = tr.comb < 0;
   }
   return w;
 }
@@ -454,16 +436,10 @@ struct RowDest {
   int64_t row;   // direct: (token, head) index into o / lse; else the partial row
 };
 
-__device__ __forceinline__ RowDest row_dest(const AttnArgs& a, const WorkItem& it, const UnitDesc& u, const Row& w) {
-  RowDest d{false, 0};
-  if (!w.ok) return d;
-  int64_t base_own, base_oth;
-  const int live_own = unit_live(a, it.unit, w.tok, w.g, it.kv, &base_own);
-  const BranchDesc br = a.branches[w.b];
-  const int oth = (u.kind == kShared) ? br.unit_pr : br.unit_sh;
-  const int live_oth = (oth >= 0) ? unit_live(a, oth, w.tok, w.g, it.kv, &base_oth) : 0;
-  d.direct = live_own + live_oth == 1;
-  d.row = d.direct ? (int64_t)w.tok * a.H_q + it.kv * a.G + w.g : base_own + (int64_t)it.split * u.bm;
+__device__ __forceinline__ RowDest row_dest(const AttnArgs& a, const WorkItem& it, const Row& w, int rloc) {
+  RowDest d;
+  d.direct = w.direct;
+  d.row = w.direct ? (int64_t)w.tok * a.H_q + it.kv * a.G + w.g : it.part_row + rloc;
   return d;
 }
 
@@ -507,48 +483,58 @@ __device__ __forceinline__ void write_row_to(const AttnArgs& a, const RowDest& d
 }
 
 template <class C, typename T, int D>
-__device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it, const UnitDesc& u,
-                                          const Row& w, float m, float l, const f32x16_t* o,
-                                          int db0, int db1, bool write_scalars, int h) {
+__device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it, const Row& w, int rloc,
+                                          float m, float l, const f32x16_t* o, int db0, int db1,
+                                          bool write_scalars, int h) {
   if (!w.ok) return;
-  write_row_to<C, T, D>(a, row_dest(a, it, u, w), true, m, l, o, db0, db1, write_scalars, h);
+  write_row_to<C, T, D>(a, row_dest(a, it, w, rloc), true, m, l, o, db0, db1, write_scalars, h);
 }
 
 // ------------------------------------------------------- combination ----
-// Log-sum-exp combination of the split-KV partials of output row (tok, kv,
-// g), d values d0 .. d0 + 3 (ADR-0060 GQA fused attention, §4: m = max m_i,
-// weights 2^(m_i - m), one normalisation at the end). Partials are folded in
-// a fixed order -- prefix shards, then suffix shards -- with the same online
-// rule as the tile loop, so the result does not depend on which item does
-// it. Rows with a single partial were written by their item directly.
-template <typename T, int D, int U>
-__device__ __forceinline__ void combine_row(const AttnArgs& a, int tok, int kv, int g, int d0) {
-  // U: partial loads in flight per fold step (the partials come from other
-  // XCDs, so each step costs a full memory round trip)
-  const int b = branch_of(a.branches, 0, a.n_branches, tok);
-  const BranchDesc br = a.branches[b];
-  int64_t base[2] = {0, 0};
-  int live[2] = {0, 0}, bm[2] = {0, 0};
-  if (br.unit_sh >= 0) {
-    live[0] = unit_live(a, br.unit_sh, tok, g, kv, &base[0]);
-    bm[0] = a.units[br.unit_sh].bm;
-  }
-  if (br.unit_pr >= 0) {
-    live[1] = unit_live(a, br.unit_pr, tok, g, kv, &base[1]);
-    bm[1] = a.units[br.unit_pr].bm;
-  }
-  const int n = live[0] + live[1];
-  if (n < 2) return;
-  float M = kNegInf, L = 0.f;
-  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q0 = 0; q0 < n; q0 += U) {
+// Log-sum-exp combination of the split-KV partials of an output row (tok,
+// kv, g) (ADR-0060 GQA fused attention, §4: m = max m_i, weights
+// 2^(m_i - m), one normalisation at the end). A row's partials are taken in
+// a fixed order -- prefix shards, then suffix shards -- so the result does
+// not depend on which workgroup combines it. Rows with a single partial
+// were written by their item directly.
+
+// Workspace row of partial q of row (g, kv) of a token with combination
+// record c: the prefix unit's shards first, then the suffix unit's.
+__device__ __forceinline__ int64_t part_of(const CombTok& c, int kv, int g, int q) {
+  const bool pre = q < c.live[0];
+  const int64_t p = pre ? c.p[0] : c.p[1];
+  const int live = pre ? c.live[0] : c.live[1], bm = pre ? c.bm[0] : c.bm[1];
+  const int sh = pre ? q : q - c.live[0];
+  return p + ((int64_t)kv * live + sh) * bm + g;
+}
+
+// (M, L, O) <- the combination of (M, L, O) and (M2, L2, O2), in that order.
+__device__ __forceinline__ void join_state(float& M, float& L, float4& O, float M2, float L2, const float4& O2) {
+  const float Mn = fmaxf(M, M2);
+  const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+  const float sa = exp2_fast(M - Mu), sb = exp2_fast(M2 - Mu);
+  L = L * sa + L2 * sb;
+  O.x = O.x * sa + O2.x * sb;
+  O.y = O.y * sa + O2.y * sb;
+  O.z = O.z * sa + O2.z * sb;
+  O.w = O.w * sa + O2.w * sb;
+  M = Mn;
+}
+
+// Folds partials [q_begin, q_end) of row (g, kv) into (M, L, O) for the d
+// values d0 .. d0 + 3, one after another; U partial loads are issued before
+// they are consumed.
+template <int D, int U>
+__device__ __forceinline__ void fold_parts(const AttnArgs& a, const CombTok& c, int kv, int g, int q_begin, int q_end,
+                                           int d0, float& M, float& L, float4& O) {
+  for (int q0 = q_begin; q0 < q_end; q0 += U) {
     float2 ml[U];
     float4 v[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int q = q0 + k;
-      if (q < n) {
-        const int64_t p = (q < live[0]) ? base[0] + (int64_t)q * bm[0] : base[1] + (int64_t)(q - live[0]) * bm[1];
+      if (q < q_end) {
+        const int64_t p = part_of(c, kv, g, q);
         ml[k] = a.part_ml[p];
         v[k] = *(const float4*)(a.part_o + p * D + d0);
       } else {
@@ -557,18 +543,15 @@ __device__ __forceinline__ void combine_row(const AttnArgs& a, int tok, int kv, 
       }
     }
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const float Mn = fmaxf(M, ml[k].x);
-      const float Mu = (Mn == kNegInf) ? 0.f : Mn;
-      const float sa = exp2_fast(M - Mu), sb = exp2_fast(ml[k].x - Mu);
-      L = L * sa + ml[k].y * sb;
-      O.x = O.x * sa + v[k].x * sb;
-      O.y = O.y * sa + v[k].y * sb;
-      O.z = O.z * sa + v[k].z * sb;
-      O.w = O.w * sa + v[k].w * sb;
-      M = Mn;
-    }
+    for (int k = 0; k < U; ++k) join_state(M, L, O, ml[k].x, ml[k].y, v[k]);
   }
+}
+
+// O / L in the storage dtype (round to nearest even) and, from the thread
+// holding d0 = 0, LSE = ln L + M ln 2.
+template <typename T, int D>
+__device__ __forceinline__ void write_combined(const AttnArgs& a, int tok, int kv, int g, int d0, float M, float L,
+                                               const float4& O) {
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
   const int64_t orow = ((int64_t)tok * a.H_q + kv * a.G + g);
   if constexpr (std::is_same<T, uint16_t>::value) {
@@ -582,56 +565,134 @@ __device__ __forceinline__ void combine_row(const AttnArgs& a, int tok, int kv, 
   if (d0 == 0) a.lse[orow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
-// Called by every thread of a narrow-kernel workgroup once its item's rows
-// are written. Tokens whose partials all come from narrow items (decode-like
-// rows: a few rows over a long KV range cut into many shards) are combined
-// here, which spares them the separate merge launch; the MFMA-bound items
-// leave theirs to lse_merge, since a combining workgroup would stall its
-// CU. Each such token has a counter per KV head; the item that
-// brings it to the planned number of arrivals combines the token's rows.
-// Release before the increment and acquire after the winning one (device
-// scope: the XCDs' L2 caches are not coherent with each other) make every
-// other item's partials visible. The winner resets the counter, so all
-// counters are zero again when the launch ends. Work per workgroup is
-// bounded and no thread waits on another workgroup.
-// The item is read again here (through an opaque copy of its index) rather
-// than kept live across the tile loop, where its registers are needed.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void combine_if_last(const AttnArgs& a, int idx, int tid, int* won) {
-  int ix = idx;
-  asm volatile("" : "+v"(ix));
-  const WorkItem it = a.items[ix];
-  if (it.n_rows <= 0) return;
-  const int32_t* tok_need = a.tok_need;
-  int32_t* counters = a.counters;
-  const int tok0 = it.tok_begin + it.row_begin / a.G;
-  const int ntok = it.tok_begin + (it.row_begin + it.n_rows - 1) / a.G - tok0 + 1;
-  __syncthreads();   // this workgroup's partial stores are complete
+// s_waitcnt immediate: vmcnt(vm), expcnt(7), lgkmcnt(0).
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
+
+// A load of plan data (written before the launch and constant during it) at
+// a wave-uniform address, made through the constant address space so that
+// it is a scalar load: scalar loads are counted apart from vector memory
+// operations, so waiting for one never waits for K/V loads in flight.
+template <typename T>
+__device__ __forceinline__ T plan_load(const T* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(const __attribute__((address_space(4))) T*)p;
+#else
+  return *p;
+#endif
+}
+
+// In-launch combination (narrow kernels). Tokens whose partials all come
+// from narrow items (decode-like rows: a few rows over a long KV range cut
+// into many shards) are combined by the last of their items to finish,
+// which spares them the separate merge launch; the MFMA-bound items leave
+// theirs to lse_merge, since a combining workgroup would stall its CU.
+//  * At the item's start, while its K/V stream is in flight, wave 0 copies
+//    the combination records of the item's tokens into LDS (a unit goes to
+//    the narrow kernel only when all its rows fit one M-tile, so an item
+//    has at most BM rows and tokens).
+//  * After its rows are written, each such token's counter (one per KV
+//    head) is incremented; the item that brings it to the planned number of
+//    arrivals combines the token's rows. Release before the increment and
+//    acquire after the winning one (device scope: the XCDs' L2 caches are
+//    not coherent with each other) make every other item's partials
+//    visible. The winner resets the counter after its combination, so all
+//    counters are zero again when the launch ends. Work per workgroup is
+//    bounded and no thread waits on another workgroup.
+//  * Two threads share each (row, 4 d values): each folds one half of the
+//    row's partials, so a decode row's shards arrive in one round of loads,
+//    and the halves are joined through a lane exchange.
+template <int BM>
+struct CombLds {
+  CombTok rec[BM];   // per token of the item (need = 0: combined elsewhere, or one partial)
+  int won[BM];
+  int kv, tok0, ntok;
+};
+
+template <int BM>
+__device__ __forceinline__ void combine_prepare(const AttnArgs& a, const WorkItem& it, int wave, int lane,
+                                                CombLds<BM>* cl) {
+  if (wave != 0) return;
+  // The item is wave-uniform; say so, so that the loads below are scalar.
+  const int tok0 = __builtin_amdgcn_readfirstlane(it.tok_begin + it.row_begin / a.G);
+  const int ntok = __builtin_amdgcn_readfirstlane(
+      (it.n_rows > 0) ? it.tok_begin + (it.row_begin + it.n_rows - 1) / a.G - tok0 + 1 : 0);
+  for (int k = 0; k < ntok; ++k) {
+    const int ci = plan_load(&a.tok_rec[tok0 + k].comb);
+    CombTok c;
+    if (ci >= 0) {
+      const CombTok* src = a.combs + ci;   // field by field: an aggregate copy would not be scalar
+      c.p[0] = plan_load(&src->p[0]);
+      c.p[1] = plan_load(&src->p[1]);
+      c.live[0] = plan_load(&src->live[0]);
+      c.live[1] = plan_load(&src->live[1]);
+      c.bm[0] = plan_load(&src->bm[0]);
+      c.bm[1] = plan_load(&src->bm[1]);
+      c.need = plan_load(&src->need);
+      c.pad = 0;
+    } else {
+      c.p[0] = c.p[1] = 0;
+      c.live[0] = c.live[1] = 0;
+      c.bm[0] = c.bm[1] = 0;
+      c.need = 0;
+      c.pad = 0;
+    }
+    if (lane == 0) cl->rec[k] = c;
+  }
+  if (lane == 0) {
+    cl->kv = it.kv;
+    cl->tok0 = tok0;
+    cl->ntok = ntok;
+  }
+}
+
+template <typename T, int D, int NT, int BM>
+__device__ __forceinline__ void combine_if_last(const AttnArgs& a, int tid, CombLds<BM>* cl) {
+  // vmcnt counts stores too: every wave's partial stores are complete at
+  // the barrier, so the release below covers them.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __syncthreads();
+  const int kv = cl->kv, tok0 = cl->tok0, ntok = cl->ntok;
   int mine = 0;
   for (int k = tid; k < ntok; k += NT) {
-    const int tok = tok0 + k;
-    const int need = tok_need[tok];
+    const int need = cl->rec[k].need;
     int w = 0;
     if (need > 0) {
-      int* c = counters + (int64_t)tok * a.H_kv + it.kv;
+      int* c = a.counters + (int64_t)(tok0 + k) * a.H_kv + kv;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       if (atomicAdd(c, 1) == need - 1) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        atomicExch(c, 0);
         w = 1;
       }
     }
-    won[k] = w;
+    cl->won[k] = w;
     mine |= w;
   }
   if (!__syncthreads_or(mine)) return;
-  const int per_tok = a.G * (D / 4);
-  for (int x = tid; x < ntok * per_tok; x += NT) {
-    const int k = x / per_tok;
-    if (!won[k]) continue;
-    const int rem = x - k * per_tok;
-    combine_row<T, D, 16>(a, tok0 + k, it.kv, rem / (D / 4), (rem % (D / 4)) * 4);
+  const int G = a.G;
+  constexpr int TPR = D / 4;   // threads (pairs) per row
+  // Lanes 2y and 2y + 1 take (row, d0) number y; the trip count and every
+  // skip below are the same for both lanes of a pair.
+  for (int x = tid; x < 2 * ntok * G * TPR; x += NT) {
+    const int y = x >> 1, half = x & 1;
+    const int rr = y / TPR;
+    const int k = rr / G;
+    if (!cl->won[k]) continue;
+    const CombTok c = cl->rec[k];
+    const int n = c.live[0] + c.live[1];
+    const int g = rr - k * G, d0 = (y - rr * TPR) * 4;
+    const int mid = (n + 1) >> 1;
+    float M = kNegInf, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    fold_parts<D, 16>(a, c, kv, g, half ? mid : 0, half ? n : mid, d0, M, L, O);
+    const float M2 = __shfl_xor(M, 1), L2 = __shfl_xor(L, 1);
+    const float4 O2 = make_float4(__shfl_xor(O.x, 1), __shfl_xor(O.y, 1), __shfl_xor(O.z, 1), __shfl_xor(O.w, 1));
+    if (half == 0) {
+      join_state(M, L, O, M2, L2, O2);
+      write_combined<T, D>(a, tok0 + k, kv, g, d0, M, L, O);
+    }
   }
+  for (int k = tid; k < ntok; k += NT)
+    if (cl->won[k]) atomicExch(a.counters + (int64_t)(tok0 + k) * a.H_kv + kv, 0);
 }
 
 // Smallest / largest valid row position of the wave.
@@ -658,15 +719,14 @@ attn_wide(AttnArgs a) {
     // The previous item's last tile loop iteration ended with a barrier after
     // all LDS reads, so its stages may be refilled at once.
     const WorkItem it = a.items[idx];
-    const UnitDesc u = a.units[it.unit];
     const int rloc = wave * 32 + i;
-    const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
+    const Row w = row_at(a, it, rloc);
     State<C> s;
     load_q<C, T, D>(a, w, it.kv, h, s);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
     const bool wave_rows = wave * 32 < it.n_rows;
-    const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
+    const KvSrc<T> src = kv_src<T, D>(a, it, it.kv);
 
     const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;
     Stage<C> st;
@@ -677,10 +737,10 @@ attn_wide(AttnArgs a) {
       const bool more = j + 1 < nt;
       if (more) load_tile<C, T, D>(src, it.key_begin + (j + 1) * C::BN, it.key_end, tid, st);
       const int tk0 = it.key_begin + j * C::BN;       // unit-local first key of the tile
-      const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
+      const bool future = a.causal && (it.key_pos0 + tk0 > pmax);
       if (wave_rows && !future) {
         char* stg = smem + (j & 1) * C::STAGE;
-        run_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, u, tk0, it.key_end,
+        run_tile<C, T, D>((const T*)stg, (const T*)(stg + C::K_ELEMS * sizeof(T)), s, it.key_pos0, tk0, it.key_end,
                           a.causal, w.pos, pmin, a.scale_log2, i, h);
       }
       if (more) {
@@ -689,7 +749,7 @@ attn_wide(AttnArgs a) {
       }
       __syncthreads();
     }
-    write_row<C, T, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
+    write_row<C, T, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
   }
 }
 
@@ -717,9 +777,6 @@ struct DmaCfg {
   static_assert(NINST % WAVES == 0, "tile must split evenly over the waves");
   static_assert(BM == kWideRowsBf16, "planner and kernel disagree on the M-tile");
 };
-
-// s_waitcnt immediate: vmcnt(vm), expcnt(7), lgkmcnt(0).
-constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
 
 // The DMA below is issued as inline assembly, so the compiler neither counts
 // it nor inserts waits for it (its own tracking of LDS DMA cannot tell ring
@@ -980,9 +1037,9 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const Dm
 
 template <class C, int D>
 __device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLane<C>& L, State<C>& s,
-                                         const UnitDesc& u, int tk0, int key_end, int causal, int row_pos,
+                                         int key_pos0, int tk0, int key_end, int causal, int row_pos,
                                          int pmin, int pmax, bool active, float c, int i, int h) {
-  const int kpos0 = u.key_pos0 + tk0;
+  const int kpos0 = key_pos0 + tk0;
   if (!active || (causal && kpos0 > pmax)) return;   // no rows, or the tile is all-future for the wave
   const int nvalid = min(C::BN, key_end - tk0);
   const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
@@ -1016,15 +1073,14 @@ attn_wide_dma(AttnArgs a) {
     // stages are refilled.
     if (idx > bin_begin) lds_barrier();
     const WorkItem it = a.items[idx];
-    const UnitDesc u = a.units[it.unit];
-    const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, u, it.kv);
+    const KvSrc<uint16_t> src = kv_src<uint16_t, D>(a, it, it.kv);
     const int kb0 = it.key_begin, ke = it.key_end;
     const int nt = (ke - kb0 + C::BN - 1) / C::BN;
     // The first pair's DMA goes out before the row bookkeeping and Q loads.
     dma_tile_any<C, D>(src, L, wave, kb0, ke, k0, v0);
     if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
     const int rloc = wave * 32 + i;
-    const Row w = row_of(a, u, it.row_begin + rloc, rloc < it.n_rows);
+    const Row w = row_at(a, it, rloc);
     State<C> s;
     load_q<C, uint16_t, D>(a, w, it.kv, h, s);
     int pmin, pmax;
@@ -1037,11 +1093,11 @@ attn_wide_dma(AttnArgs a) {
       lds_barrier();                                                                                        \
       if (j + 2 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);                \
       if (j + 3 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);                \
-      dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, u, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax,   \
-                  active, c, i, h);                                                                         \
+      dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, it.key_pos0, kb0 + j * C::BN, ke, a.causal, w.pos, pmin,    \
+                     pmax, active, c, i, h);                                                                \
       if (j + 1 < nt)                                                                                       \
-        dma_step<C, D>(lds_u32(KB), lds_u32(VB), L, s, u, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin, \
-                    pmax, active, c, i, h);                                                                 \
+        dma_step<C, D>(lds_u32(KB), lds_u32(VB), L, s, it.key_pos0, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, \
+                       pmin, pmax, active, c, i, h);                                                        \
     }
     for (int j0 = 0; j0 < nt; j0 += 4) {
       {
@@ -1055,7 +1111,7 @@ attn_wide_dma(AttnArgs a) {
     }
 #undef GQA_DMA_PAIR
     s.l += __shfl_xor(s.l, 32);
-    write_row<C, uint16_t, D>(a, it, u, w, s.m, s.l, s.o, 0, C::OB, true, h);
+    write_row<C, uint16_t, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
   }
 }
 
@@ -1065,7 +1121,7 @@ __global__ void __launch_bounds__(256, (Cfg<T, D, true>::WAVES_PER_SIMD))
 attn_narrow(AttnArgs a) {
   using C = Cfg<T, D, true>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  __shared__ int won[C::BM];
+  __shared__ CombLds<C::BM> cl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
   for (int idx = bin_begin; idx < bin_end; ++idx) {
@@ -1073,13 +1129,13 @@ attn_narrow(AttnArgs a) {
     // stages are refilled.
     if (idx > bin_begin) __syncthreads();
     const WorkItem it = a.items[idx];
-    const UnitDesc u = a.units[it.unit];
-    const Row w = row_of(a, u, it.row_begin + i, i < it.n_rows);
+    const Row w = row_at(a, it, i);
     State<C> s;
     load_q<C, T, D>(a, w, it.kv, h, s);
+    combine_prepare(a, it, wave, lane, &cl);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
-    const KvSrc<T> src = kv_src<T, D>(a, u, it.kv);
+    const KvSrc<T> src = kv_src<T, D>(a, it, it.kv);
 
     const int nt = (it.key_end - it.key_begin + C::BN - 1) / C::BN;   // wave tiles: wave w takes w, w+4, ...
     const int rounds = (nt + 3) / 4;
@@ -1096,9 +1152,9 @@ attn_narrow(AttnArgs a) {
       if (j + 4 < nt) load_tile<C, T, D>(src, it.key_begin + (j + 4) * C::BN, it.key_end, lane, st);
       if (have) {
         const int tk0 = it.key_begin + j * C::BN;
-        const bool future = a.causal && (u.key_pos0 + tk0 > pmax);
+        const bool future = a.causal && (it.key_pos0 + tk0 > pmax);
         if (!future)
-          run_tile<C, T, D>(Ks, Vs, s, u, tk0, it.key_end, a.causal, w.pos, pmin, a.scale_log2, i, h);
+          run_tile<C, T, D>(Ks, Vs, s, it.key_pos0, tk0, it.key_end, a.causal, w.pos, pmin, a.scale_log2, i, h);
       }
       __syncthreads();
     }
@@ -1136,9 +1192,9 @@ attn_narrow(AttnArgs a) {
         for (int k = 0; k < 4; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
         acc[r] = x;
       }
-      write_row<C, T, D>(a, it, u, w, M, L, &acc, db, db + 1, wave == 0, h);
+      write_row<C, T, D>(a, it, w, i, M, L, &acc, db, db + 1, wave == 0, h);
     }
-    combine_if_last<T, D, 256>(a, idx, tid, won);
+    combine_if_last<T, D, 256>(a, tid, &cl);
   }
 }
 
@@ -1173,7 +1229,7 @@ attn_narrow_dma(AttnArgs a) {
   using C = NarrowDmaCfg<D>;
   __shared__ __attribute__((aligned(1024))) char st[C::WAVES * 2 * C::TB];   // per wave: K tile then V tile
   __shared__ float2 mml[C::WAVES * 64];
-  __shared__ int won[C::BM];
+  __shared__ CombLds<C::BM> cl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const DmaLane<C> L = dma_lane<C>(0, lane);
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
@@ -1187,30 +1243,23 @@ attn_narrow_dma(AttnArgs a) {
     const int nt = (ke - kb0 + C::BN - 1) / C::BN;
     char* K0 = st + wave * 2 * C::TB;
     char* V0 = K0 + C::TB;
-    // Q first, then the K/V stream: both need only the work item, and Q
-    // issued behind a whole shard of K/V would arrive last. The unit and
-    // branch lookups (row positions) follow under the stream.
-    const int r = it.row_begin + i;
-    Row w;
-    w.ok = i < it.n_rows;
-    w.tok = it.tok_begin + r / a.G;
-    w.g = r - (r / a.G) * a.G;
+    // The row's token record and Q first, then the K/V stream: they need
+    // only the work item, and loads issued behind a whole shard of K/V would
+    // arrive last. The combination records are copied under the stream.
+    const Row w = row_at(a, it, i);
     State<C> s;
     load_q<C, uint16_t, D>(a, w, it.kv, h, s);
     if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
-    const UnitDesc u = a.units[it.unit];
-    w = row_of(a, u, r, w.ok);
-    // The output lookups (unit, tile and branch records) are dependent
-    // loads: resolve them now, under the K/V stream, not after the merge.
-    const RowDest dst = row_dest(a, it, u, w);
+    combine_prepare(a, it, wave, lane, &cl);
+    const RowDest dst = row_dest(a, it, w, i);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
     const bool active = it.n_rows > 0;
     const float c = a.scale_log2;
     for (int j = wave; j < nt; j += C::WAVES) {
       wait_dma<0>();
-      dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, u, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax, active, c,
-                     i, h);
+      dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, it.key_pos0, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax,
+                     active, c, i, h);
       if (j + C::WAVES < nt) {
         wait_dma<63>();   // own LDS reads of the stage done
         dma_tile_any<C, D>(src, L, 0, kb0 + (j + C::WAVES) * C::BN, ke, K0, V0);
@@ -1255,82 +1304,35 @@ attn_narrow_dma(AttnArgs a) {
       }
       write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
     }
-    combine_if_last<uint16_t, D, 512>(a, idx, tid, won);
+    combine_if_last<uint16_t, D, 512>(a, tid, &cl);
   }
 }
 
 // --------------------------------------------------------------- merge ----
 // One workgroup per (query token, KV head); each thread owns 4 consecutive
 // d values of one of the G rows. Tokens whose partials all come from the
-// narrow kernel were combined there (combine_if_last) and are skipped. Partials are folded in a fixed order
-// (prefix shards, then suffix shards) with the same online rule as the
-// tile loop, so the result is bitwise repeatable (ADR-0060 GQA fused
-// attention, §4: m = max m_i, weights exp(m_i - m), normalise once at the
-// end). Loads of several partials are issued before they are consumed.
+// narrow kernel were combined there (combine_if_last) and are skipped.
+// Partials are folded in a fixed order (prefix shards, then suffix shards)
+// with the same online rule as the tile loop, so the result is bitwise
+// repeatable (ADR-0060 GQA fused attention, §4: m = max m_i, weights
+// exp(m_i - m), normalise once at the end). Loads of several partials are
+// issued before they are consumed.
 template <typename T, int D, int U>
 __global__ void __launch_bounds__(256)
 lse_merge(AttnArgs a) {
   const int tok = blockIdx.x / a.H_kv, kv = blockIdx.x - tok * a.H_kv;
-  if (a.tok_need[tok] > 0) return;
+  const int ci = a.tok_rec[tok].comb;
+  if (ci < 0) return;                    // single partial: written by the attention kernel
+  const CombTok c = a.combs[ci];
+  if (c.need > 0) return;                // combined inside the narrow launch
   constexpr int TPR = D / 4;   // threads per row
-  const int b = branch_of(a.branches, 0, a.n_branches, tok);
-  const BranchDesc br = a.branches[b];
+  const int n = c.live[0] + c.live[1];
   for (int g = threadIdx.x / TPR; g < a.G; g += 256 / TPR) {
     const int d0 = (threadIdx.x % TPR) * 4;
-    int64_t base[2] = {0, 0};
-    int live[2] = {0, 0}, bm[2] = {0, 0};
-    if (br.unit_sh >= 0) {
-      live[0] = unit_live(a, br.unit_sh, tok, g, kv, &base[0]);
-      bm[0] = a.units[br.unit_sh].bm;
-    }
-    if (br.unit_pr >= 0) {
-      live[1] = unit_live(a, br.unit_pr, tok, g, kv, &base[1]);
-      bm[1] = a.units[br.unit_pr].bm;
-    }
-    const int n = live[0] + live[1];
-    if (n < 2) continue;   // written directly by the attention kernel
     float M = kNegInf, L = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q0 = 0; q0 < n; q0 += U) {
-      float2 ml[U];
-      float4 v[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int q = q0 + k;
-        if (q < n) {
-          const int64_t p = (q < live[0]) ? base[0] + (int64_t)q * bm[0]
-                                          : base[1] + (int64_t)(q - live[0]) * bm[1];
-          ml[k] = a.part_ml[p];
-          v[k] = *(const float4*)(a.part_o + p * D + d0);
-        } else {
-          ml[k] = make_float2(kNegInf, 0.f);
-          v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const float Mn = fmaxf(M, ml[k].x);
-        const float Mu = (Mn == kNegInf) ? 0.f : Mn;
-        const float sa = exp2_fast(M - Mu), sb = exp2_fast(ml[k].x - Mu);
-        L = L * sa + ml[k].y * sb;
-        O.x = O.x * sa + v[k].x * sb;
-        O.y = O.y * sa + v[k].y * sb;
-        O.z = O.z * sa + v[k].z * sb;
-        O.w = O.w * sa + v[k].w * sb;
-        M = Mn;
-      }
-    }
-    const float inv = (L > 0.f) ? 1.f / L : 0.f;
-    const int64_t orow = ((int64_t)tok * a.H_q + kv * a.G + g);
-    if constexpr (std::is_same<T, uint16_t>::value) {
-      uint2 pk;
-      pk.x = pack_bf16x2(O.x * inv, O.y * inv);
-      pk.y = pack_bf16x2(O.z * inv, O.w * inv);
-      *(uint2*)((uint16_t*)a.o + orow * D + d0) = pk;
-    } else {
-      *(float4*)((float*)a.o + orow * D + d0) = make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
-    }
-    if (d0 == 0) a.lse[orow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
+    fold_parts<D, U>(a, c, kv, g, 0, n, d0, M, L, O);
+    write_combined<T, D>(a, tok, kv, g, d0, M, L, O);
   }
 }
 

@@ -16,17 +16,14 @@ struct AttnArgs {
   const int32_t* page_table;
   const WorkItem* items;
   const int32_t* bins;  // workgroup b runs items [bins[b], bins[b+1])
-  const UnitDesc* units;
-  const BranchDesc* branches;
-  const TileInfo* tiles;
-  const int32_t* tok_need;  // per query token: narrow items whose arrival completes it (0: not combined in-launch)
+  const TokRec* tok_rec;    // per query token
+  const CombTok* combs;     // per token whose rows have two or more partials
   int32_t* counters;        // [n_q_tokens, H_kv] arrival counters, zero between launches
   float* part_o;        // [part_rows, D] unnormalised partial O
   float2* part_ml;      // [part_rows] (m in log2 units, l)
   void* o;              // [n_q_tokens, H_q, D] storage dtype
   float* lse;           // [n_q_tokens, H_q]
   int32_t max_pages;
-  int32_t n_branches;
   int32_t H_q;
   int32_t H_kv;
   int32_t G;

@@ -163,6 +163,8 @@ std::string validate_plan_input(const PlanInput& in) {
   if (in.H_q <= 0 || in.H_kv <= 0) return "num_q_heads and num_kv_heads must be > 0";
   if (in.H_q % in.H_kv != 0) return "num_q_heads must be a multiple of num_kv_heads";
   if (in.D != 64 && in.D != 128) return "head_dim must be 64 or 128";
+  if (in.H_q / in.H_kv > ((in.dtype == 0) ? kWideRowsBf16 : kWideRows))
+    return "too many query heads per KV head for one M-tile";
   if (in.page_size <= 0 || in.page_size > 4096) return "page_size must be in 1..4096";
   const size_t ng = in.g_start.size(), nb = in.b_group.size();
   if (in.g_len.size() != ng) return "group arrays differ in length";
@@ -214,7 +216,6 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     d.ctx_len = in.g_len[in.b_group[b]] + in.b_priv[b];
     d.unit_sh = d.unit_pr = -1;
     d.group = in.b_group[b];
-    d.pad0 = d.pad1 = 0;
     for (int32_t t = 0; t < d.q_len; ++t) pos_of_tok.push_back(d.ctx_len - d.q_len + t);
     q_acc += d.q_len;
     P->max_branch_pages = std::max<int32_t>(P->max_branch_pages,
@@ -265,20 +266,22 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     P->units.push_back(u);
   }
 
-  // M-tiles and their causal key clamp.
+  // M-tiles (whole tokens: bm / G of them, so every row of a token shares
+  // one M-tile of each unit) and their causal key clamp.
   const int32_t nu = (int32_t)P->units.size();
   std::vector<UnitWork> uw(nu);
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
     const int64_t M = (int64_t)u.n_tok * G;
     u.bm = (M <= kNarrowRows) ? kNarrowRows : wide_rows;
-    const int32_t ntile = (int32_t)ceil_div(M, u.bm);
+    u.tpt = u.bm / G;
+    const int32_t ntile = (int32_t)ceil_div(u.n_tok, u.tpt);
     uw[ui].unit = ui;
     uw[ui].tile_key_end.resize(ntile);
     for (int32_t t = 0; t < ntile; ++t) {
-      const int64_t r0 = (int64_t)t * u.bm, r1 = std::min<int64_t>(M, r0 + u.bm);
+      const int64_t t0 = (int64_t)t * u.tpt, t1 = std::min<int64_t>(u.n_tok, t0 + u.tpt);
       int32_t pmax = -1;
-      for (int64_t tok = u.tok_begin + r0 / G; tok <= u.tok_begin + (r1 - 1) / G; ++tok)
+      for (int64_t tok = u.tok_begin + t0; tok < u.tok_begin + t1; ++tok)
         pmax = std::max(pmax, pos_of_tok[tok]);
       int64_t kend = u.key_len;
       if (in.causal) kend = std::min<int64_t>(u.key_len, std::max<int64_t>(0, (int64_t)pmax - u.key_pos0 + 1));
@@ -336,10 +339,9 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           const UnitDesc& u = P->units[ui];
           const int32_t s = (int32_t)ceil_div(u.key_len, chunk);
           std::vector<int32_t> bnd = shard_bounds(u.key_len, s, kWideKeys);
-          const int64_t M = (int64_t)u.n_tok * G;
           for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
             const int32_t kend = uw[ui].tile_key_end[t];
-            const int64_t rows = std::min<int64_t>(u.bm, M - (int64_t)t * u.bm);
+            const int64_t rows = std::min<int64_t>(u.tpt, u.n_tok - (int64_t)t * u.tpt) * G;
             int live = 0;
             for (size_t k = 0; k + 1 < bnd.size(); ++k) {
               if (bnd[k] >= kend) break;
@@ -374,7 +376,6 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     P->api_splits[api_slot[ui]] = u.n_splits;
     P->max_splits = std::max(P->max_splits, u.n_splits);
     u.tile_off = (int32_t)P->tiles.size();
-    const int64_t M = (int64_t)u.n_tok * G;
     for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
       const int32_t kend = uw[ui].tile_key_end[t];
       int32_t live = 0;
@@ -384,8 +385,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       ti.part_off = part;
       part += (int64_t)in.H_kv * live * u.bm;
       P->tiles.push_back(ti);
-      const int32_t row_begin = (int32_t)(t * u.bm);
-      const int32_t n_rows = (int32_t)std::min<int64_t>(u.bm, M - row_begin);
+      const int32_t row_begin = (int32_t)(t * u.tpt * G);
+      const int32_t n_rows = (int32_t)std::min<int64_t>(u.tpt, u.n_tok - (int64_t)t * u.tpt) * G;
       for (int32_t s = 0; s < live; ++s) {
         for (int32_t kv = 0; kv < in.H_kv; ++kv) {
           WorkItem w{};
@@ -400,7 +401,9 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           w.kind = u.kind;
           w.src = u.src;
           w.tok_begin = u.tok_begin;
-          w.pad = 0;
+          w.key_pos0 = u.key_pos0;
+          w.part_row = ti.part_off + ((int64_t)kv * live + s) * u.bm;
+          w.pad0 = w.pad1 = 0;
           P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
           (u.bm != kNarrowRows ? P->wide : P->narrow).push_back(w);
         }
@@ -423,46 +426,42 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   bin_items(&P->wide, in.wide_per_cu * in.n_cu, in.n_cu, &P->wide_bins);
   bin_items(&P->narrow, in.narrow_per_cu * in.n_cu, in.n_cu, &P->narrow_bins);
 
-  // Output rows that need combining (two or more live partials). A token
-  // whose partials all come from narrow items is combined by the last of
-  // them to finish: tok_need counts those of every M-tile that holds one of
-  // the token's G rows, in both of its units. Any other token with such rows
-  // goes to the merge kernel.
-  P->tok_need.assign(P->n_q_tokens, 0);
+  // Per-token records. All G rows of a token lie in one M-tile of each of
+  // its units, so they have the same partials: live shards of that tile in
+  // the prefix unit plus in the suffix unit. Tokens whose rows have two or
+  // more get a combination record. A token whose partials all come from
+  // narrow items is combined by the last of them to finish (need = the
+  // number of such items per KV head); any other goes to the merge kernel.
+  P->tok_rec.assign(P->n_q_tokens, TokRec{0, -1});
+  P->combs.clear();
   for (int32_t b = 0; b < nb; ++b) {
     const BranchDesc& br = P->branches[b];
     for (int32_t t = 0; t < br.q_len; ++t) {
       const int32_t tok = br.q_begin + t;
-      bool any = false;
-      for (int32_t g = 0; g < G; ++g) {
-        int32_t n = 0;
-        for (int32_t ui : {br.unit_sh, br.unit_pr}) {
-          if (ui < 0) continue;
-          const UnitDesc& u = P->units[ui];
-          const int64_t r = (int64_t)(tok - u.tok_begin) * G + g;
-          n += P->tiles[u.tile_off + r / u.bm].live;
-        }
-        if (n >= 2) {
-          P->merge_rows += in.H_kv;
-          any = true;
-        }
-        P->max_row_parts = std::max(P->max_row_parts, n);
-      }
-      if (!any) continue;
-      int32_t items = 0;
+      TokRec& tr = P->tok_rec[tok];
+      tr.pos = pos_of_tok[tok];
+      CombTok c{};
+      int32_t n = 0;
       bool narrow_only = true;
-      for (int32_t ui : {br.unit_sh, br.unit_pr}) {
-        if (ui < 0) continue;
-        const UnitDesc& u = P->units[ui];
-        const int64_t r0 = (int64_t)(tok - u.tok_begin) * G, r1 = r0 + G - 1;
-        for (int64_t tl = r0 / u.bm; tl <= r1 / u.bm; ++tl) {
-          const int32_t live = P->tiles[u.tile_off + tl].live;
-          items += live;
-          if (live > 0 && u.bm != kNarrowRows) narrow_only = false;
-        }
+      const int32_t us[2] = {br.unit_sh, br.unit_pr};
+      for (int x = 0; x < 2; ++x) {
+        if (us[x] < 0) continue;
+        const UnitDesc& u = P->units[us[x]];
+        const int32_t tl = (tok - u.tok_begin) / u.tpt;
+        const TileInfo& ti = P->tiles[u.tile_off + tl];
+        c.p[x] = ti.part_off + (int64_t)(tok - u.tok_begin - tl * u.tpt) * G;
+        c.live[x] = ti.live;
+        c.bm[x] = u.bm;
+        n += ti.live;
+        if (ti.live > 0 && u.bm != kNarrowRows) narrow_only = false;
       }
-      if (narrow_only) P->tok_need[tok] = items;
-      else P->merge_launch = true;
+      P->max_row_parts = std::max(P->max_row_parts, n);
+      if (n < 2) continue;
+      P->merge_rows += (int64_t)G * in.H_kv;
+      c.need = narrow_only ? n : 0;
+      if (!narrow_only) P->merge_launch = true;
+      tr.comb = (int32_t)P->combs.size();
+      P->combs.push_back(c);
     }
   }
   return "";

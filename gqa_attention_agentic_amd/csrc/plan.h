@@ -42,11 +42,8 @@ struct Plan {
   int64_t n_kv_tiles = 0;           // (item, KV tile) pairs
   int64_t merge_rows = 0;           // output rows with two or more partials
   int32_t max_row_parts = 0;        // largest partial count of any output row
-  // Per query token: when at least one of its rows has two or more
-  // partials and every item writing them runs in the narrow kernel, how
-  // many such items there are per KV head (the last of them to finish
-  // combines the token inside the launch); else 0.
-  std::vector<int32_t> tok_need;
+  std::vector<TokRec> tok_rec;      // per query token
+  std::vector<CombTok> combs;       // per token whose rows have two or more partials
   bool merge_launch = false;        // some row is left to the separate merge kernel
   int32_t max_splits = 0;
   int32_t n_q_tokens = 0;

@@ -8,11 +8,18 @@
 // GQA fold of ADR-0060 GQA fused attention, §5.2: the M dimension of both
 // products is (token, g), so one K/V tile serves all of them.
 //
-// A unit's rows are cut into M-tiles of `bm` rows and its keys into
-// `n_splits` shards (ADR-0060, §4 split-and-combine). A *work item* is one
-// (unit, KV head, M-tile, shard); each produces an (m, l, O) partial per row,
-// or the final O / LSE directly when that row has exactly one live partial
-// (ADR-0060, §0.5.4, N = 1).
+// A unit's rows are cut into M-tiles of whole tokens (at most `bm` rows)
+// and its keys into `n_splits` shards (ADR-0060, §4 split-and-combine). A
+// *work item* is one (unit, KV head, M-tile, shard); each produces an
+// (m, l, O) partial per row, or the final O / LSE directly when that row has
+// exactly one live partial (ADR-0060, §0.5.4, N = 1).
+//
+// Everything a kernel needs about its rows is precomputed here (ADR-0060,
+// §7: the issuing side owns control, the kernel is handed bases and
+// counts): the work item carries its unit's fields and its workspace row,
+// and one record per query token gives the token's position and, when its
+// rows have several partials, where they are. A kernel therefore issues no
+// chain of dependent metadata loads.
 #pragma once
 #include <stdint.h>
 
@@ -26,6 +33,7 @@ constexpr int kNarrowKeys = 32;   // keys per KV tile and wave, narrow kernel
 
 enum UnitKind : int32_t { kShared = 0, kPrivate = 1 };
 
+// Host-side unit record (the kernels see its fields through the items).
 struct UnitDesc {
   int32_t kind;        // UnitKind
   int32_t tok_begin;   // first query token of the unit (index into q)
@@ -33,12 +41,12 @@ struct UnitDesc {
   int32_t src;         // shared: first token of the prefix in k_shared; private: branch id
   int32_t key_len;     // keys in the unit
   int32_t key_pos0;    // context position of the unit's key 0
-  int32_t bm;          // rows per M-tile (kWideRows or kNarrowRows)
+  int32_t bm;          // row stride of an M-tile (kWideRows[Bf16] or kNarrowRows)
+  int32_t tpt;         // query tokens per M-tile: bm / G (an M-tile holds whole tokens)
   int32_t tile_off;    // index of the unit's first M-tile in the tile table
   int32_t branch_lo;   // branches whose tokens form the unit: [branch_lo, branch_hi)
   int32_t branch_hi;
   int32_t n_splits;    // shards of the key range
-  int32_t pad;
 };
 
 struct BranchDesc {
@@ -48,15 +56,13 @@ struct BranchDesc {
   int32_t unit_sh;     // unit index of the group's prefix, -1 if none
   int32_t unit_pr;     // unit index of the private suffix, -1 if none
   int32_t group;
-  int32_t pad0, pad1;
 };
 
-// Per M-tile of a unit: how many of the unit's shards are live for the
-// tile (shards are in key order and liveness under causality is a prefix),
-// and where the tile's partials start in the workspace.
+// Per M-tile of a unit (host side): how many of the unit's shards are live
+// for the tile (shards are in key order and liveness under causality is a
+// prefix), and where the tile's partials start in the workspace.
 struct TileInfo {
   int32_t live;        // live shards
-  int32_t pad;
   int64_t part_off;    // first partial row; row layout: ((kv * live + s) * bm + r_in_tile)
 };
 
@@ -69,11 +75,34 @@ struct WorkItem {
   int32_t key_end;
   int32_t split;       // shard index (partial slot)
   int32_t tile;        // M-tile index within the unit
-  // Copies of the unit's kind, src and tok_begin, so that the Q loads and
-  // the K/V stream can be issued before the unit record arrives.
+  // Copies of the unit's fields, so that nothing but this record is needed
+  // before the Q loads and the K/V stream go out.
   int32_t kind;
   int32_t src;
   int32_t tok_begin;
+  int32_t key_pos0;
+  int64_t part_row;    // workspace row of the item's row 0 (its row r: part_row + r)
+  int32_t pad0, pad1;
+};
+
+// Per query token.
+struct TokRec {
+  int32_t pos;         // context position of the token
+  int32_t comb;        // index into the combination records, or -1 when each
+                       // of its rows has a single partial (written directly)
+};
+
+// Where the partials of a token's rows are, for a token whose rows have two
+// or more: for its group-prefix unit (0) and its private-suffix unit (1),
+// row (tok, g) of KV head kv has shard s at workspace row
+// p[x] + (kv * live[x] + s) * bm[x] + g. The rows are combined in the narrow
+// launch when need > 0 (the number of narrow items per KV head that write
+// them; the last to finish combines), otherwise by the merge kernel.
+struct CombTok {
+  int64_t p[2];
+  int32_t live[2];
+  int32_t bm[2];
+  int32_t need;
   int32_t pad;
 };
 

@@ -77,7 +77,9 @@ typedef struct gqa_attn gqa_attn;   /* opaque: plan buffers, workspace, timers *
 
 /* Create a handle for fixed head geometry and dtype. `p` (host) is copied.
  * Errors: GQA_ERR_INVALID_ARG for bad parameters, GQA_ERR_UNSUPPORTED for a
- * head_dim other than 64/128, GQA_ERR_HIP if no HIP device is usable. */
+ * head_dim other than 64/128 or more than 256 (bf16) / 128 (fp32) query
+ * heads per KV head (the rows of one token must fit one M-tile of the
+ * MFMA kernel), GQA_ERR_HIP if no HIP device is usable. */
 gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out);
 
 /* One attention forward over a set of groups and branches.

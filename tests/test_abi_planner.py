@@ -107,6 +107,11 @@ def test_items_partition_visible_pairs(w):
     assert len(got) == len(set(got)), "a visible pair is covered twice"
     assert set(got) == _expected_pairs(w)
     assert stats["n_items_wide"] + stats["n_items_narrow"] == len(items)
+    # A unit on the 32-row kernel fits one M-tile, so a narrow item's tokens
+    # hold at most 32 rows (the size of that kernel's combination table).
+    for (_slot, _kv, r0, nr, _k0, _k1, _split, kern, _bin) in items:
+        if kern == 1:
+            assert r0 == 0 and nr <= 32
 
 
 def test_split_override_honoured():
@@ -227,6 +232,34 @@ def test_bad_params_rejected(kw, msg):
     with pytest.raises(_lib.GqaError) as e:
         G.plan_host(args["H_q"], args["H_kv"], args["d"], args["page_size"], [0], [10], [0], [1], [0], True)
     assert msg in str(e.value)
+
+
+@pytest.mark.parametrize("dtype,h_q,ok", [("bf16", 256, True), ("bf16", 512, False),
+                                           ("fp32", 128, True), ("fp32", 256, False)])
+def test_query_heads_per_kv_head_limit(dtype, h_q, ok):
+    """An M-tile holds whole tokens, so one KV head serves at most as many
+    query heads as the MFMA kernel has rows (256 bf16, 128 fp32); more is
+    reported as unsupported."""
+    def call():
+        return G.plan_host(h_q, 1, 128, 16, [0], [500], [0], [3], [0], True, dtype=dtype)
+    if ok:
+        items, _, _ = call()
+        assert items and all(r0 % h_q == 0 and nr % h_q == 0 for (_, _, r0, nr, *_rest) in items)
+    else:
+        with pytest.raises(_lib.GqaError) as e:
+            call()
+        assert e.value.status == -2 and "query heads per KV head" in str(e.value)
+
+
+def test_m_tiles_hold_whole_tokens():
+    """With G = 3 a 256-row tile would split a token; tiles hold 85 tokens
+    (255 rows) instead, so every row of a token shares one M-tile."""
+    w = custom("g3", H_q=6, H_kv=2, shared=(300,), branches=((0, 100, 50), (0, 90, 20)), seed=1)
+    items, _, _ = _plan(w)
+    assert items
+    for (_slot, _kv, r0, nr, *_rest) in items:
+        assert r0 % 3 == 0 and nr % 3 == 0 and nr <= 255
+    assert set(_covered_pairs(w, items)) == _expected_pairs(w)
 
 
 @pytest.mark.parametrize("meta,msg", [

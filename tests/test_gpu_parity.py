@@ -49,6 +49,9 @@ SMALL = {
                              seed=110),
     "gqa_g16": lambda: custom("gqa_g16", H_q=32, H_kv=2, d=128, shared=(200,),
                               branches=((0, 2, 10), (0, 3, 10)), seed=111),
+    "gqa_g3_whole_token_tiles": lambda: custom("gqa_g3_whole_token_tiles", H_q=6, H_kv=2, d=128,
+                                               shared=(300,), branches=((0, 100, 50), (0, 90, 20)),
+                                               seed=117),
     "prefill_private_only": lambda: custom("prefill_private_only", shared=(0,), branches=((0, 50, 50),),
                                            seed=112),
     "queries_reach_into_prefix": lambda: custom("queries_reach_into_prefix", shared=(100,),
