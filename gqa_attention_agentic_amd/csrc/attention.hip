@@ -766,6 +766,7 @@ template <int D>
 struct DmaCfg {
   static constexpr bool BF16 = true;
   static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;        // launch size (every launch and occupancy query uses it)
   static constexpr int BM = 32 * WAVES;             // rows per item
   static constexpr int BN = 64;                     // keys per tile
   static constexpr int ROW = D * 2;                 // bytes per key row
@@ -1054,7 +1055,7 @@ __device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLa
 // and the waves sharing a SIMD may drift apart by up to a tile between
 // barriers.
 template <int D>
-__global__ void __launch_bounds__(512, 2)
+__global__ void __launch_bounds__(DmaCfg<D>::THREADS, 2)
 attn_wide_dma(AttnArgs a) {
   using C = DmaCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k0[C::TB];
@@ -1211,6 +1212,7 @@ template <int D>
 struct NarrowDmaCfg {
   static constexpr bool BF16 = true;
   static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;        // launch size (every launch and occupancy query uses it)
   static constexpr int BM = kNarrowRows;
   static constexpr int BN = 32;                     // keys per wave tile
   static constexpr int ROW = D * 2;
@@ -1224,7 +1226,7 @@ struct NarrowDmaCfg {
 };
 
 template <int D>
-__global__ void __launch_bounds__(512, 2)
+__global__ void __launch_bounds__(NarrowDmaCfg<D>::THREADS, 2)
 attn_narrow_dma(AttnArgs a) {
   using C = NarrowDmaCfg<D>;
   __shared__ __attribute__((aligned(1024))) char st[C::WAVES * 2 * C::TB];   // per wave: K tile then V tile
@@ -1304,7 +1306,7 @@ attn_narrow_dma(AttnArgs a) {
       }
       write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
     }
-    combine_if_last<uint16_t, D, 512>(a, tid, &cl);
+    combine_if_last<uint16_t, D, C::THREADS>(a, tid, &cl);
   }
 }
 
@@ -1344,10 +1346,10 @@ hipError_t launch_attn_t(const AttnArgs& a, int32_t n_bins, bool narrow, hipStre
                          hipEvent_t e1) {
   if (n_bins <= 0) return hipSuccess;
   if (narrow) {
-    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_bins, 512);
+    if constexpr (std::is_same<T, uint16_t>::value) GQA_LAUNCH((attn_narrow_dma<D>), n_bins, NarrowDmaCfg<D>::THREADS);
     else GQA_LAUNCH((attn_narrow<T, D>), n_bins, 256);
   } else if constexpr (std::is_same<T, uint16_t>::value) {
-    GQA_LAUNCH((attn_wide_dma<D>), n_bins, 512);
+    GQA_LAUNCH((attn_wide_dma<D>), n_bins, DmaCfg<D>::THREADS);
   } else {
     GQA_LAUNCH((attn_wide<T, D>), n_bins, 256);
   }
@@ -1360,11 +1362,11 @@ hipError_t occupancy_t(bool narrow, int* per_cu) {
   hipError_t e;
   if (narrow) {
     if constexpr (std::is_same<T, uint16_t>::value)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow_dma<D>, 512, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow_dma<D>, NarrowDmaCfg<D>::THREADS, 0);
     else
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_narrow<T, D>, 256, 0);
   } else if constexpr (std::is_same<T, uint16_t>::value) {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_wide_dma<D>, 512, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_wide_dma<D>, DmaCfg<D>::THREADS, 0);
   } else {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_wide<T, D>, 256, 0);
   }
