@@ -42,7 +42,8 @@ class PlanStats(ctypes.Structure):
     _fields_ = [("n_items_wide", ctypes.c_int64), ("n_items_narrow", ctypes.c_int64),
                 ("n_kv_tiles", ctypes.c_int64), ("n_merge_rows", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("n_units", ctypes.c_int64),
-                ("max_splits", ctypes.c_int32), ("merge_launch", ctypes.c_int32)]
+                ("max_splits", ctypes.c_int32), ("merge_launch", ctypes.c_int32),
+                ("wide_cus", ctypes.c_int32), ("narrow_cus", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -2,12 +2,18 @@
 //
 // A forward call validates its arguments on the host, builds (or reuses) the
 // plan, copies it to the device through pinned staging with one async copy,
-// and launches up to three kernels on the caller's stream: the 128-row
-// attention kernel, the 32-row attention kernel and the LSE merge. It never
-// synchronises the stream; the only allocations happen when the plan or the
-// partial workspace outgrows what the handle already holds.
+// and launches up to three kernels: the MFMA-bound (wide) attention kernel,
+// the 32-row (narrow) attention kernel and the LSE merge, all ordered on the
+// caller's stream. When a forward has items of both attention kernels, the
+// narrow one runs on the handle's side stream, forked from and joined back
+// into the caller's stream with events, so that the two run side by side on
+// the compute units the plan gives each. It never synchronises the stream;
+// the only allocations happen when the plan or the partial workspace
+// outgrows what the handle already holds (and the side stream and its two
+// events, created at the first forward that needs them).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -38,7 +44,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // events around the kernel's execution.
 struct TimerSlot {
   hipEvent_t ev[6];   // wide start/end, narrow start/end, merge start/end
-  bool wide, narrow, merged;
+  bool wide, narrow, merged, concurrent;
 };
 
 }  // namespace
@@ -64,6 +70,9 @@ struct gqa_attn {
   char* d_work = nullptr;
   bool counters_dirty = true;   // counters must be cleared before the next launch
   size_t d_work_cap = 0;
+  // side stream for the narrow kernel when both attention kernels run
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   // timing
   bool timing = false;
   std::vector<TimerSlot> timers;
@@ -129,6 +138,8 @@ void fill_stats(const gqa::Plan& P, int64_t D, gqa_plan_stats* s) {
   s->n_units = (int64_t)P.units.size();
   s->max_splits = P.max_splits;
   s->merge_launch = P.merge_launch ? 1 : 0;
+  s->wide_cus = P.wide_cus;
+  s->narrow_cus = P.narrow_cus;
 }
 
 // Serialised plan: wide items | narrow items | wide bins | narrow bins |
@@ -277,6 +288,9 @@ gqa_status gqa_attn_destroy(gqa_attn* h) {
   if (h->d_work) hipFree(h->d_work);
   if (h->h_staging) hipHostFree(h->h_staging);
   if (h->staging_free) hipEventDestroy(h->staging_free);
+  if (h->side) hipStreamDestroy(h->side);
+  if (h->fork) hipEventDestroy(h->fork);
+  if (h->join) hipEventDestroy(h->join);
   for (auto& t : h->timers)
     for (auto& ev : t.ev) hipEventDestroy(ev);
   delete h;
@@ -398,15 +412,43 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
     tm->wide = !Q.wide.empty();
     tm->narrow = !Q.narrow.empty();
     tm->merged = Q.merge_launch;
+    tm->concurrent = Q.concurrent;
   }
-  if (!Q.wide.empty()) {
+  if (Q.concurrent) {
+    // Narrow kernel on the side stream, after everything already queued on
+    // the caller's stream (plan upload, counter clear); the caller's stream
+    // waits for it before the merge. Both streams have the default priority.
+    if (!h->side) {
+      e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "side stream creation");
+    }
+    e = hipEventRecord(h->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "fork to the side stream");
+    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
+    a.bins = (const int32_t*)(h->d_plan + h->off_narrow_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, h->side,
+                              ev(2), ev(3));
+    if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
+    e = hipEventRecord(h->join, h->side);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(join)");
+    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
+    a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
+                              ev(1));
+    if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
+    e = hipStreamWaitEvent(st, h->join, 0);
+    if (e != hipSuccess) return hip_fail(e, "join from the side stream");
+  } else if (!Q.wide.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
     a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);
     e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
                               ev(1));
     if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
   }
-  if (!Q.narrow.empty()) {
+  if (!Q.concurrent && !Q.narrow.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
     a.bins = (const int32_t*)(h->d_plan + h->off_narrow_bins);
     e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, st, ev(2),
@@ -453,9 +495,26 @@ gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
       if (!used[j]) continue;
       hipError_t e = hipEventSynchronize(t.ev[2 * j + 1]);
       if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    }
+    for (int j = 0; j < 3; ++j) {
+      if (!used[j] || (t.concurrent && j == 1)) continue;
       float ms = 0.f;
-      e = hipEventElapsedTime(&ms, t.ev[2 * j], t.ev[2 * j + 1]);
-      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      hipError_t e;
+      if (t.concurrent && j == 0) {
+        // Side by side: the span from the earlier start to the later end,
+        // i.e. the largest (end - start) over the four pairs.
+        float best = 0.f;
+        for (int s0 : {0, 2})
+          for (int s1 : {1, 3}) {
+            e = hipEventElapsedTime(&ms, t.ev[s0], t.ev[s1]);
+            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+            best = std::max(best, ms);
+          }
+        ms = best;
+      } else {
+        e = hipEventElapsedTime(&ms, t.ev[2 * j], t.ev[2 * j + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      }
       (j < 2 ? at : mg) += ms;
     }
   }

@@ -157,6 +157,44 @@ void bin_items(std::vector<WorkItem>* items, int slots, int n_cu, std::vector<in
   *items = std::move(out);
 }
 
+// A forward with both MFMA-bound (wide) and KV-bandwidth-bound (narrow)
+// items runs the two attention kernels side by side on disjoint sets of
+// compute units: the narrow items need only part of the chip to stream at
+// HBM speed, and the wide ones compute on the rest. With one resident
+// workgroup per CU for each kernel, both grids are resident at once. The
+// split (a multiple of the XCD count, so that both grids stay evenly spread
+// over the XCDs) is the one for which the later of the two is predicted to
+// finish first:
+//   wide:   (M-tile, key) pairs / wide CUs x time per key of an M-tile;
+//   narrow: the larger of (K/V bytes / HBM bandwidth) and (K/V bytes /
+//           narrow CUs / one CU's streaming rate).
+// It is decided before the shard counts, which then fill each share.
+// The rates are fitted to runs of the two kernels side by side with forced
+// splits (one MI355X): a 256-row bf16 M-tile costs ~31 ns per key, a CU of
+// the narrow kernel streams ~35 GB/s of K/V, HBM sustains ~5.5 TB/s.
+constexpr double kWideNsPerKeyBf16 = 31.0;
+constexpr double kHbmBytesPerNs = 5500.0;
+constexpr double kCuBytesPerNs = 35.0;
+
+void split_cus(double wide_keys, double narrow_keys, const PlanInput& in, int32_t* wide_cus, int32_t* narrow_cus) {
+  const int esize = (in.dtype == 0) ? 2 : 4;
+  // fp32: half the rows per M-tile at 1/16 of the matrix rate.
+  const double wide_ns_per_key = (in.dtype == 0) ? kWideNsPerKeyBf16 : kWideNsPerKeyBf16 * 8.0;
+  const double bytes_n = narrow_keys * 2.0 * in.D * esize;
+  double best = 1e300;
+  *narrow_cus = kXcds;
+  for (int32_t c = kXcds; c <= in.n_cu - kXcds; c += kXcds) {
+    const double tw = wide_keys * wide_ns_per_key / (in.n_cu - c);
+    const double tn = std::max(bytes_n / kHbmBytesPerNs, bytes_n / (c * kCuBytesPerNs));
+    const double t = std::max(tw, tn);
+    if (t < best) {
+      best = t;
+      *narrow_cus = c;
+    }
+  }
+  *wide_cus = in.n_cu - *narrow_cus;
+}
+
 }  // namespace
 
 std::string validate_plan_input(const PlanInput& in) {
@@ -289,6 +327,21 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     }
   }
 
+  // Compute units of each attention kernel (see split_cus).
+  {
+    double wk = 0.0, nk = 0.0;
+    for (int32_t ui = 0; ui < nu; ++ui)
+      for (int32_t kend : uw[ui].tile_key_end)
+        (P->units[ui].bm == kNarrowRows ? nk : wk) += (double)kend * in.H_kv;
+    P->wide_cus = P->narrow_cus = in.n_cu;
+    P->concurrent = false;
+    if (wk > 0.0 && nk > 0.0 && in.wide_per_cu == 1 && in.narrow_per_cu == 1 && in.n_cu % kXcds == 0 &&
+        in.n_cu >= 2 * kXcds) {
+      split_cus(wk, nk, in, &P->wide_cus, &P->narrow_cus);
+      P->concurrent = true;
+    }
+  }
+
   // Split counts: the caller's override, else the heuristic below.
   std::vector<int32_t> S(nu, 0);
   auto override_of = [&](int32_t ui) -> int32_t {
@@ -298,8 +351,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   // stream into about one item per resident workgroup slot, no shard below
   // 256 keys, so every slot streams a similar number of bytes (ADR-0060,
   // §5.2-§5.3: decode is bound by KV loads).
-  const int64_t slots = 2LL * std::max(1, in.narrow_per_cu) * in.n_cu;   // about two items per resident workgroup
-  const int64_t wide_slots = (int64_t)std::max(1, in.wide_per_cu) * in.n_cu;
+  const int64_t slots = 2LL * std::max(1, in.narrow_per_cu) * P->narrow_cus;   // about two items per resident workgroup
+  const int64_t wide_slots = (int64_t)std::max(1, in.wide_per_cu) * P->wide_cus;
   {
     int64_t wn = 0;
     for (int32_t ui = 0; ui < nu; ++ui)
@@ -423,8 +476,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   };
   std::stable_sort(P->wide.begin(), P->wide.end(), by_cost);
   std::stable_sort(P->narrow.begin(), P->narrow.end(), by_cost);
-  bin_items(&P->wide, in.wide_per_cu * in.n_cu, in.n_cu, &P->wide_bins);
-  bin_items(&P->narrow, in.narrow_per_cu * in.n_cu, in.n_cu, &P->narrow_bins);
+  bin_items(&P->wide, in.wide_per_cu * P->wide_cus, P->wide_cus, &P->wide_bins);
+  bin_items(&P->narrow, in.narrow_per_cu * P->narrow_cus, P->narrow_cus, &P->narrow_bins);
 
   // Per-token records. All G rows of a token lie in one M-tile of each of
   // its units, so they have the same partials: live shards of that tile in

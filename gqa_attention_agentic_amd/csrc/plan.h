@@ -45,6 +45,10 @@ struct Plan {
   std::vector<TokRec> tok_rec;      // per query token
   std::vector<CombTok> combs;       // per token whose rows have two or more partials
   bool merge_launch = false;        // some row is left to the separate merge kernel
+  // Both kernels have items and run side by side on disjoint sets of compute
+  // units (wide_cus + narrow_cus = the device's); else each gets all of them.
+  bool concurrent = false;
+  int32_t wide_cus = 0, narrow_cus = 0;
   int32_t max_splits = 0;
   int32_t n_q_tokens = 0;
   int32_t n_shared_tokens = 0;

@@ -37,6 +37,10 @@
  * Calls are stream-ordered and asynchronous: gqa_attn_forward returns without
  * waiting for the GPU. Host arrays may be reused as soon as a call returns.
  * One handle serves one stream at a time; concurrent calls on one handle race.
+ * A forward with both decode-like and MFMA-bound work runs part of it on a
+ * side stream that the handle owns (default priority), forked from and
+ * joined back into the caller's stream with events; the forward's work is
+ * still complete when the caller's stream reaches the point after the call.
  * Every entry point returns a gqa_status; on a negative status nothing was
  * launched and gqa_attn_last_error() holds a message (thread-local).
  */
@@ -146,6 +150,10 @@ typedef struct {
   int32_t merge_launch;       /* 1 if the forward makes a separate merge launch;
                                  0 when every row with several partials is
                                  combined inside the narrow attention launch */
+  int32_t wide_cus;           /* compute units given to each attention kernel:  */
+  int32_t narrow_cus;         /* both the device's count, unless the forward has
+                                 items of both kernels, which then run side by
+                                 side on disjoint CUs (wide + narrow = device) */
 } gqa_plan_stats;
 gqa_status gqa_attn_plan_stats(const gqa_attn* h, gqa_plan_stats* out);
 
@@ -159,7 +167,9 @@ gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n);
  * stop events). enable != 0 starts recording (and clears earlier records).
  * gqa_attn_kernel_times waits for the recorded events and returns the summed
  * milliseconds of every forward since timing was enabled -- attn_ms sums the
- * attention launches (wide and narrow), merge_ms the separate merge launch --
+ * attention launches (wide and narrow; when the two run side by side, the
+ * span from the earlier start to the later end), merge_ms the separate
+ * merge launch --
  * and the number of forwards, then clears the records. Rows whose partials
  * all come from the narrow (decode-like) kernel are combined inside that
  * launch, so their merge time is part of attn_ms; a forward with no other

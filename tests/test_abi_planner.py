@@ -218,6 +218,24 @@ def test_merge_launch_only_when_wide_partials(name, launch):
     assert stats["merge_launch"] == launch
 
 
+@pytest.mark.parametrize("name,split", [("decode_8k", False), ("fanout_8x20_32k", False),
+                                        ("prefill_32k", False), ("mixed_32dec_64x4", True)])
+def test_side_by_side_split(name, split):
+    """A forward with items of both attention kernels gives each a disjoint
+    share of the 256 CUs (a multiple of the 8 XCDs), and each kernel's items
+    are dealt to at most that many workgroups; otherwise each kernel gets
+    the whole device."""
+    items, _, stats = _plan(get_workload(name))
+    if split:
+        assert stats["wide_cus"] + stats["narrow_cus"] == 256
+        assert stats["wide_cus"] % 8 == 0 and 8 <= stats["narrow_cus"] <= 248
+    else:
+        assert stats["wide_cus"] == stats["narrow_cus"] == 256
+    for kern, cus in ((0, stats["wide_cus"]), (1, stats["narrow_cus"])):
+        bins = {it[8] for it in items if it[7] == kern}
+        assert len(bins) <= cus and (not bins or max(bins) < cus)
+
+
 BAD = [
     (dict(H_q=6, H_kv=4), "multiple"),
     (dict(d=96), "head_dim"),
