@@ -1,8 +1,8 @@
 // Split-KV GQA flash attention for gfx950 (CDNA4), bf16 or fp32.
 //
-// Per work item (unit, KV head, M-tile, KV shard) a workgroup of 4 waves
-// runs the FlashAttention tile loop of ADR-0060 GQA fused attention (TL;DR
-// kernel and §3 per-tile op sequence) on the rows of its M-tile:
+// Per work item (unit, KV head, M-tile, KV shard) a workgroup runs the
+// FlashAttention tile loop of ADR-0060 GQA fused attention (TL;DR kernel
+// and §3 per-tile op sequence) on the rows of its M-tile, 32 rows per wave:
 //
 //   S^T = K Q^T * scale      v_mfma_f32_32x32x16_bf16 (fp32: 32x32x2_f32)
 //   mask                     only in tiles that cross the causal diagonal or
@@ -24,18 +24,22 @@
 //  * The S^T registers are already the B operand of V^T P^T (the contraction
 //    index order is free as long as both operands agree), so P never leaves
 //    registers.
-//  * V is transposed while it is staged into LDS (V^T rows of BN keys, keys
-//    permuted inside each 16-key chunk so that one 16-byte LDS read yields a
-//    lane's 8 operand values). K stays [key][d] with a padded pitch.
-//  * Wide kernel (MFMA-bound fan-out / prefill): 128 rows, 4 waves x 32 rows,
-//    64-key K/V^T tiles double-buffered in LDS, the next tile's global loads
-//    in flight while the current one is computed.
-//  * Narrow kernel (KV-bandwidth-bound decode, <= 32 rows): every wave
-//    streams its own 32-key tiles with the next one prefetched in registers;
-//    the 4 per-wave (m, l, O) states are merged through LDS at the end.
+//  * bf16 kernels stage K and V tiles into LDS with global->LDS DMA, rows
+//    unpadded and XOR-swizzled per 16-byte chunk; V^T operands come from a
+//    transposing LDS read. The fp32 kernels stage through registers (V is
+//    transposed on the store, K rows padded).
+//  * Wide kernels (MFMA-bound fan-out / prefill): bf16 256 rows (8 waves, a
+//    4-stage ring of 64-key tiles consumed in pairs), fp32 128 rows (4
+//    waves, double-buffered).
+//  * Narrow kernels (KV-bandwidth-bound decode, <= 32 rows): every wave
+//    streams its own 32-key tiles; the per-wave (m, l, O) states are merged
+//    through LDS at the end, and tokens whose partials all come from narrow
+//    items are combined inside the launch by the last item to finish.
 //  * A row with exactly one live partial in total writes O / l and LSE
 //    directly (ADR-0060, §0.5.4 N = 1); otherwise the unnormalised partial
-//    (m, l, O) goes to the workspace for the merge kernel (§4).
+//    (m, l, O) goes to the workspace for the combination (§4).
+//  * Every workgroup runs the items of one bin (planned per resident
+//    workgroup) back to back.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>

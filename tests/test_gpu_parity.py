@@ -168,6 +168,31 @@ def test_alternating_plans_on_one_handle():
                 first[w.name] = (o.clone(), lse.clone())
 
 
+def test_side_by_side_kernels_join_the_callers_stream():
+    """A forward with items of both attention kernels runs them side by side
+    (the narrow one on the handle's side stream) on a split of the CUs. The
+    caller's stream must still see the finished result: copies queued right
+    after the forward on the same non-default stream match the oracle, and
+    the kernel timing reports one forward."""
+    w = SMALL["mixed_bf16"]()
+    inp = generate(w, "cuda")
+    ref = H.oracle_rows(w, inp)
+    h = H.handle_for(w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    h.enable_timing(True)
+    with torch.cuda.stream(s):
+        o, lse = h.forward_inputs(inp, w.causal, splits=w.splits, stream=s.cuda_stream)
+        o_copy, lse_copy = o.clone(), lse.clone()
+    s.synchronize()
+    stats = h.plan_stats()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert stats["wide_cus"] + stats["narrow_cus"] == n_cu and 0 < stats["narrow_cus"] < n_cu
+    attn_ms, _, n = h.kernel_times()
+    assert n == 1 and attn_ms > 0
+    H.compare(w, o_copy, lse_copy, ref[0], ref[1], ref[2], label="side by side")
+
+
 def test_causal_future_keys_ignored():
     """Garbage (NaN) in keys after every query position never reaches O."""
     w = custom("future", shared=(200,), branches=((0, 64, 0),), seed=118)
