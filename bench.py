@@ -37,7 +37,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E (published)
 LLC_BYTES = 256 << 20           # Infinity Cache
 
 WORKLOADS = {"fanout": "fanout_8x20_32k", "decode": "decode_8k", "prefill": "prefill_32k",
-             "mixed": "mixed_32dec_64x4", "tiny": "tiny_fp32_fanout"}
+             "mixed": "mixed_32dec_64x4", "tiny": "tiny_fp32_fanout", "join400": "join_400_32k",
+             "join8000": "join_8000_32k"}
 KERNEL_SOURCES = ["gqa_attention_agentic_amd/csrc/attention.hip"]
 
 
@@ -228,7 +229,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fanout", choices=sorted(WORKLOADS))
-    ap.add_argument("--others", default="decode,prefill,mixed",
+    ap.add_argument("--others", default="decode,prefill,mixed,join400,join8000",
                     help="comma list of secondary workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -265,7 +266,7 @@ def main():
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         # Long workloads get fewer timed steps, so the default run stays short.
-        long_wl = name in ("prefill", "mixed")
+        long_wl = name in ("prefill", "mixed", "join8000")
         wo, ro = run_workload(WORKLOADS[name], max(3, args.steps // 4) if long_wl else args.steps, 2, log)
         ro["roofline"] = roofline_of(wo, ro, traffic_for(wo))
         others[name] = ro

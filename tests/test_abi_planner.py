@@ -97,6 +97,7 @@ CASES = [
     custom("reach", H_q=4, H_kv=2, shared=(100,), branches=((0, 30, 10),), seed=1),
     custom("noncausal", H_q=4, H_kv=2, shared=(257,), branches=((0, 2, 3),), causal=False, seed=1,
            splits=[5, 2]),
+    custom("join", H_q=8, H_kv=2, shared=(500,), branches=((0, 70, 70),), seed=1),
 ]
 
 

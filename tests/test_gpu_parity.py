@@ -61,6 +61,8 @@ SMALL = {
     "zero_q_len_branch": lambda: custom("zero_q_len_branch", shared=(90,),
                                         branches=((0, 3, 10), (0, 0, 20), (0, 2, 5)), seed=115),
     "single_key": lambda: custom("single_key", shared=(1,), branches=((0, 1, 0),), seed=116),
+    "join_continuation": lambda: custom("join_continuation", shared=(700,), branches=((0, 60, 60),),
+                                        seed=118),
 }
 
 
@@ -257,3 +259,17 @@ def test_mixed_32dec_64x4_sampled():
         qb.append(qb[-1] + b.q_len)
     toks = [qb[b] for b in dec] + [qb[b] + t for b in fan for t in (0, 3)]
     _sample_parity("mixed_32dec_64x4", dec + fan, toks)
+
+
+def test_join_400_32k_sampled():
+    """Continuation prefill after a join: the new tokens see the whole prefix
+    and the join input up to themselves."""
+    toks = [0, 1, 15, 16, 31, 32, 199, 398, 399]
+    _sample_parity("join_400_32k", [0], toks)
+
+
+@pytest.mark.timeout(600)
+def test_join_8000_32k_sampled():
+    rng = random.Random(7)
+    toks = {0, 1, 31, 32, 63, 64, 4095, 4096, 7999} | {rng.randrange(8000) for _ in range(3)}
+    _sample_parity("join_8000_32k", [0], sorted(toks))

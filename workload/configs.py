@@ -184,8 +184,25 @@ def mixed_32dec_64x4() -> Workload:
                   description="32 decodes with lengths U{1024..65536} + 64 x 4 fan-out over 65536 prefix")
 
 
+def join_400_32k() -> Workload:
+    """Main-agent continuation prefill after a schema-constrained join
+    (AHBM Agentic Runtime Architecture, §5.4 and §5.6): 8 sub-agent results
+    of 50 tokens each, 400 join-input tokens, appended in 16-token pages
+    after the 32768-token shared prefix and prefilled causally (their
+    queries are the whole new suffix)."""
+    return _llama("join_400_32k", [Group(32768)], [Branch(0, 400, 400)], causal=True, seed=6,
+                  description="join prefill: 400 join-input tokens over a 32768-token shared prefix")
+
+
+def join_8000_32k() -> Workload:
+    """The same after a full-text join (§5.5): 8 x 1000 = 8000 join-input
+    tokens over the 32768-token shared prefix."""
+    return _llama("join_8000_32k", [Group(32768)], [Branch(0, 8000, 8000)], causal=True, seed=7,
+                  description="join prefill: 8000 join-input tokens over a 32768-token shared prefix")
+
+
 WORKLOADS = {f.__name__: f for f in (tiny_fp32_fanout, decode_8k, fanout_8x20_32k, prefill_32k,
-                                      mixed_32dec_64x4)}
+                                      mixed_32dec_64x4, join_400_32k, join_8000_32k)}
 
 
 def get_workload(name: str) -> Workload:
