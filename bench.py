@@ -148,6 +148,60 @@ def run_workload(name: str, steps: int, warmup: int, log):
     return w, res
 
 
+def run_append(steps: int, warmup: int, log):
+    """Times the paged K/V append of a full-text join's 8000 new rows (AHBM
+    Agentic Runtime Architecture, §5.5) into one branch's private pages:
+    HBM-bound, each row's K and V read once and written once. Input copies
+    rotate over more than twice the Infinity Cache."""
+    import torch
+
+    import gqa_attention_agentic_amd as G
+    from workload import get_workload
+
+    w = get_workload("join_8000_32k")
+    rows, H_kv, d, ps = 8000, w.num_kv_heads, w.head_dim, w.page_size
+    n_pages = -(-rows // ps)
+    row_bytes = 2 * H_kv * d * 2                 # K and V, bf16
+    moved = 2 * rows * row_bytes                 # read + written
+    n_copies = max(1, min(16, -(-2 * LLC_BYTES // (moved))))
+    g = torch.Generator(device="cuda").manual_seed(8)
+    sets = []
+    for _ in range(n_copies):
+        kn = torch.randn(rows, H_kv, d, generator=g, device="cuda").to(torch.bfloat16)
+        vn = torch.randn(rows, H_kv, d, generator=g, device="cuda").to(torch.bfloat16)
+        kp = torch.empty(n_pages, H_kv, ps, d, dtype=torch.bfloat16, device="cuda")
+        vp = torch.empty_like(kp)
+        table = torch.randperm(n_pages, generator=g, device="cuda").to(torch.int32).view(1, -1).contiguous()
+        sets.append((kn, vn, kp, vp, table))
+    h = G.GqaAttention(w.num_q_heads, H_kv, d, ps, w.dtype)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kn, vn, kp, vp, table = sets[i % n_copies]
+        h.append_kv(kn, vn, kp, vp, table, [0], [rows], stream=stream.cuda_stream)
+
+    for i in range(max(warmup, n_copies)):
+        step(i)
+    torch.cuda.synchronize()
+    h.enable_timing(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kms, n = h.append_times()
+    h.enable_timing(False)
+    kms /= max(1, n)
+    gbps = moved / (kms * 1e-3) / 1e9
+    log(f"[bench] append 8000 rows: {ms * 1e3:.1f} us/call wall, kernel {kms * 1e3:.1f} us, {gbps:.0f} GB/s")
+    return {"workload": "append_kv: 8000 rows (join input) into 16-token pages", "ms_per_step": ms,
+            "kernel_ms": kms, "bytes_per_call": moved, "input_copies": n_copies,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": gbps / PEAK_HBM_GBPS, "traffic": None}}
+
+
 def roofline_of(w, res, traffic):
     """Roofline of the dominant kernel (attention) from its HIP-event time."""
     t = res["attn_kernel_ms"] * 1e-3
@@ -229,7 +283,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fanout", choices=sorted(WORKLOADS))
-    ap.add_argument("--others", default="decode,prefill,mixed,join400,join8000",
+    ap.add_argument("--others", default="decode,prefill,mixed,join400,join8000,append",
                     help="comma list of secondary workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -265,6 +319,9 @@ def main():
     traffic = traffic_for(w)
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
+        if name == "append":
+            others[name] = run_append(args.steps, 2, log)
+            continue
         # Long workloads get fewer timed steps, so the default run stays short.
         long_wl = name in ("prefill", "mixed", "join8000")
         wo, ro = run_workload(WORKLOADS[name], max(3, args.steps // 4) if long_wl else args.steps, 2, log)

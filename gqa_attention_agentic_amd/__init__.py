@@ -107,6 +107,35 @@ class GqaAttention:
                             inp.branch_q_len, inp.branch_private_len, causal, splits=splits,
                             out=out, lse=lse, stream=stream)
 
+    def append_kv(self, k_new, v_new, k_pages, v_pages, page_table, branch_private_len: Sequence[int],
+                  branch_n_new: Sequence[int], stream=None) -> None:
+        """Appends k_new / v_new ([rows, H_kv, d], branch b's branch_n_new[b]
+        rows contiguous, branches in order) to the branches' private pages,
+        after their branch_private_len[b] existing tokens (gqa_attn_append_kv)."""
+        import torch
+        want = torch.bfloat16 if self.dtype_code == _lib.GQA_BF16 else torch.float32
+        dev = k_pages.get_device()
+        for name, t in (("k_new", k_new), ("v_new", v_new), ("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.dtype != want or t.get_device() != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {want} tensor on {k_pages.device}")
+        if page_table.dtype != torch.int32 or page_table.get_device() != dev or not page_table.is_contiguous():
+            raise ValueError("page_table must be a contiguous int32 tensor on the same device")
+        nb = len(branch_n_new)
+        if len(branch_private_len) != nb or (page_table.dim() == 2 and page_table.shape[0] < nb):
+            raise ValueError("branch_private_len, branch_n_new and page_table rows must cover the same branches")
+        if tuple(k_new.shape) != (sum(branch_n_new), self.num_kv_heads, self.head_dim) or v_new.shape != k_new.shape:
+            raise ValueError("k_new / v_new must be [sum(branch_n_new), num_kv_heads, head_dim]")
+        if (k_pages.dim() != 4 or tuple(k_pages.shape[1:]) != (self.num_kv_heads, self.page_size, self.head_dim)
+                or v_pages.shape != k_pages.shape):
+            raise ValueError("k_pages / v_pages must be [n_pages, num_kv_heads, page_size, head_dim]")
+        if stream is None:
+            stream = torch.cuda.current_stream(k_pages.device).cuda_stream
+        ptr = lambda t: t.data_ptr() if t.numel() > 0 else None
+        _lib.check(self.lib.gqa_attn_append_kv(
+            self._h, ptr(k_new), ptr(v_new), ptr(k_pages), ptr(v_pages), k_pages.shape[0], ptr(page_table),
+            page_table.shape[1] if page_table.dim() == 2 else 0, nb, _lib.int_array(branch_private_len),
+            _lib.int_array(branch_n_new), stream))
+
     # ------------------------------------------------------- introspection --
     def plan_stats(self) -> dict:
         s = _lib.PlanStats()
@@ -126,6 +155,12 @@ class GqaAttention:
         a, m, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
         _lib.check(self.lib.gqa_attn_kernel_times(self._h, ctypes.byref(a), ctypes.byref(m), ctypes.byref(n)))
         return a.value, m.value, n.value
+
+    def append_times(self):
+        """(append kernel ms, appends) summed since timing was enabled."""
+        m, n = ctypes.c_double(), ctypes.c_int64()
+        _lib.check(self.lib.gqa_attn_append_times(self._h, ctypes.byref(m), ctypes.byref(n)))
+        return m.value, n.value
 
     def close(self) -> None:
         if getattr(self, "_h", None):

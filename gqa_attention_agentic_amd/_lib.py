@@ -27,7 +27,7 @@ GQA_FP32 = 1
 EXPORTED = (
     "gqa_attn_create", "gqa_attn_forward", "gqa_attn_destroy", "gqa_attn_last_error",
     "gqa_attn_plan_stats", "gqa_attn_plan_splits", "gqa_attn_enable_timing",
-    "gqa_attn_kernel_times", "gqa_attn_plan_host",
+    "gqa_attn_kernel_times", "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times",
 )
 
 
@@ -82,9 +82,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gqa_attn_plan_host.argtypes = [ctypes.POINTER(Params), I32, I32P, I32P, I32, I32P, I32P, I32P,
                                        I32P, I32, I32P, I64, ctypes.POINTER(I64), I32P,
                                        ctypes.POINTER(PlanStats)]
+    lib.gqa_attn_append_kv.argtypes = [P, VP, VP, VP, VP, I32, VP, I32, I32, I32P, I32P, VP]
+    lib.gqa_attn_append_times.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]
     for name in ("gqa_attn_create", "gqa_attn_forward", "gqa_attn_destroy", "gqa_attn_plan_stats",
                  "gqa_attn_plan_splits", "gqa_attn_enable_timing", "gqa_attn_kernel_times",
-                 "gqa_attn_plan_host"):
+                 "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib

@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <vector>
 
@@ -70,6 +71,20 @@ struct gqa_attn {
   char* d_work = nullptr;
   bool counters_dirty = true;   // counters must be cleared before the next launch
   size_t d_work_cap = 0;
+  // K/V append: per-row (branch, position) list on the device, and a ring
+  // of pinned staging slots, each with the event after which it may be
+  // rewritten (the host waits only for the upload of four calls back)
+  int2* d_rows = nullptr;
+  size_t d_rows_cap = 0;
+  struct RowSlot {
+    int2* h = nullptr;
+    size_t cap = 0;
+    hipEvent_t free = nullptr;
+  } row_slots[4];
+  int row_next = 0;
+  std::vector<int32_t> rows_key;   // (private_len, n_new) per branch of the list now on the device
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> append_timers;   // start/stop of timed appends
+  size_t append_timed = 0;
   // side stream for the narrow kernel when both attention kernels run
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -289,6 +304,15 @@ gqa_status gqa_attn_destroy(gqa_attn* h) {
   if (h->h_staging) hipHostFree(h->h_staging);
   if (h->staging_free) hipEventDestroy(h->staging_free);
   if (h->side) hipStreamDestroy(h->side);
+  if (h->d_rows) hipFree(h->d_rows);
+  for (auto& rs : h->row_slots) {
+    if (rs.h) hipHostFree(rs.h);
+    if (rs.free) hipEventDestroy(rs.free);
+  }
+  for (auto& t : h->append_timers) {
+    hipEventDestroy(t.first);
+    hipEventDestroy(t.second);
+  }
   if (h->fork) hipEventDestroy(h->fork);
   if (h->join) hipEventDestroy(h->join);
   for (auto& t : h->timers)
@@ -462,6 +486,140 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   return GQA_OK;
 }
 
+namespace {
+
+// Row list of an append -- (branch, position in its private suffix) per new
+// row -- through the next pinned staging slot to the device.
+gqa_status upload_rows(gqa_attn* h, int32_t n_branches, const int32_t* branch_private_len,
+                       const int32_t* branch_n_new, int64_t n_rows, hipStream_t st) {
+  hipError_t e;
+  // This staging slot may still feed the copy of four calls back.
+  auto& rs = h->row_slots[h->row_next];
+  if (rs.free) {
+    e = hipEventSynchronize(rs.free);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  } else {
+    e = hipEventCreateWithFlags(&rs.free, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if ((size_t)n_rows > rs.cap) {
+    if (rs.h) hipHostFree(rs.h);
+    rs.h = nullptr;
+    rs.cap = 0;
+    e = hipHostMalloc((void**)&rs.h, (size_t)n_rows * sizeof(int2), hipHostMallocDefault);
+    if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "pinned row-list staging allocation failed");
+    rs.cap = (size_t)n_rows;
+  }
+  if ((size_t)n_rows > h->d_rows_cap) {
+    if (h->d_rows) {
+      e = hipFree(h->d_rows);   // synchronises the device: no kernel still reads it
+      if (e != hipSuccess) return hip_fail(e, "hipFree(rows)");
+    }
+    h->d_rows = nullptr;
+    h->d_rows_cap = 0;
+    e = hipMalloc((void**)&h->d_rows, (size_t)n_rows * sizeof(int2));
+    if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "row-list allocation failed");
+    h->d_rows_cap = (size_t)n_rows;
+  }
+  int64_t r = 0;
+  for (int32_t b = 0; b < n_branches; ++b)
+    for (int32_t i = 0; i < branch_n_new[b]; ++i) rs.h[r++] = make_int2(b, branch_private_len[b] + i);
+  e = hipMemcpyAsync(h->d_rows, rs.h, (size_t)n_rows * sizeof(int2), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipEventRecord(rs.free, st);
+  if (e != hipSuccess) return hip_fail(e, "row-list upload");
+  h->row_next = (h->row_next + 1) % 4;
+  return GQA_OK;
+}
+
+}  // namespace
+
+gqa_status gqa_attn_append_kv(gqa_attn* h, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                              int32_t n_pages, const int32_t* page_table, int32_t max_pages_per_branch,
+                              int32_t n_branches, const int32_t* branch_private_len, const int32_t* branch_n_new,
+                              void* stream) {
+  if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  if (n_branches < 0 || n_pages < 0 || max_pages_per_branch < 0)
+    return fail(GQA_ERR_INVALID_ARG, "negative branch, page or page-table size");
+  if (n_branches > 0 && (!branch_private_len || !branch_n_new))
+    return fail(GQA_ERR_INVALID_ARG, "branch arrays are NULL");
+  const int64_t ps = h->p.page_size;
+  int64_t n_rows = 0;
+  for (int32_t b = 0; b < n_branches; ++b) {
+    if (branch_private_len[b] < 0 || branch_n_new[b] < 0)
+      return fail(GQA_ERR_INVALID_ARG, "branch " + std::to_string(b) + ": negative length");
+    if ((int64_t)branch_private_len[b] + branch_n_new[b] > (int64_t)max_pages_per_branch * ps)
+      return fail(GQA_ERR_INVALID_ARG, "branch " + std::to_string(b) + ": appended rows exceed its page table");
+    n_rows += branch_n_new[b];
+  }
+  if (n_rows > std::numeric_limits<int32_t>::max()) return fail(GQA_ERR_INVALID_ARG, "too many rows");
+  if (n_rows == 0) return GQA_OK;
+  if (!k_new || !v_new || !k_pages || !v_pages || !page_table || n_pages == 0)
+    return fail(GQA_ERR_INVALID_ARG, "NULL tensor or empty page pool");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages))
+    return fail(GQA_ERR_INVALID_ARG, "K/V tensors must be 16-byte aligned");
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  // The row list is uploaded only when it differs from the one already on
+  // the device (stream order keeps that one valid for this launch).
+  std::vector<int32_t> key(2 * (size_t)n_branches);
+  for (int32_t b = 0; b < n_branches; ++b) {
+    key[2 * b] = branch_private_len[b];
+    key[2 * b + 1] = branch_n_new[b];
+  }
+  if (key != h->rows_key) {
+    h->rows_key.clear();
+    gqa_status s = upload_rows(h, n_branches, branch_private_len, branch_n_new, n_rows, st);
+    if (s != GQA_OK) return s;
+    h->rows_key = std::move(key);
+  }
+  gqa::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.page_table = page_table;
+  a.rows = h->d_rows;
+  a.max_pages = max_pages_per_branch;
+  a.n_pages = n_pages;
+  a.page_size = h->p.page_size;
+  a.num_kv_heads = h->p.num_kv_heads;
+  a.row_bytes = h->p.head_dim * (h->p.dtype == GQA_BF16 ? 2 : 4);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (h->timing) {
+    if (h->append_timed == h->append_timers.size()) {
+      hipEvent_t x = nullptr, y = nullptr;
+      e = hipEventCreate(&x);
+      if (e == hipSuccess) e = hipEventCreate(&y);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      h->append_timers.emplace_back(x, y);
+    }
+    e0 = h->append_timers[h->append_timed].first;
+    e1 = h->append_timers[h->append_timed].second;
+    ++h->append_timed;
+  }
+  e = gqa::launch_append(a, (int32_t)n_rows, st, e0, e1);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_append_times(gqa_attn* h, double* ms, int64_t* n_calls) {
+  if (!h || !ms || !n_calls) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  double t = 0.0;
+  for (size_t k = 0; k < h->append_timed; ++k) {
+    hipError_t e = hipEventSynchronize(h->append_timers[k].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float x = 0.f;
+    e = hipEventElapsedTime(&x, h->append_timers[k].first, h->append_timers[k].second);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    t += x;
+  }
+  *ms = t;
+  *n_calls = (int64_t)h->append_timed;
+  h->append_timed = 0;
+  return GQA_OK;
+}
+
 gqa_status gqa_attn_plan_stats(const gqa_attn* h, gqa_plan_stats* out) {
   if (!h || !out) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
   if (!h->have_plan) return fail(GQA_ERR_INVALID_ARG, "no forward has been planned on this handle");
@@ -482,6 +640,7 @@ gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable) {
   if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
   h->timing = enable != 0;
   h->timers_used = 0;
+  h->append_timed = 0;
   return GQA_OK;
 }
 

@@ -55,4 +55,23 @@ hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_part
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 
+// Append of new K and V rows to branches' private pages (append.hip).
+struct AppendArgs {
+  const void* k_new;        // [n_rows, H_kv, d]
+  const void* v_new;
+  void* k_pages;            // [n_pages, H_kv, page_size, d]
+  void* v_pages;
+  const int32_t* page_table;  // [n_branches, max_pages]
+  const int2* rows;         // per appended row: (branch, position in its private suffix)
+  int32_t max_pages;
+  int32_t n_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t row_bytes;        // d x element size (a multiple of 16)
+  int32_t pad;
+};
+
+hipError_t launch_append(const AppendArgs& p, int32_t n_rows, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
+
 }  // namespace gqa

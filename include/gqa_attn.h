@@ -132,6 +132,36 @@ gqa_status gqa_attn_forward(gqa_attn* h,
                             void* o, float* lse,
                             void* stream);
 
+/* Append new K and V rows to branches' private pages: the step before a
+ * forward that attends to them. A branch's context is its group's shared
+ * prefix (referenced, never copied) followed by its private pages, filled
+ * slot after slot (AHBM Agentic Runtime Architecture, §3.1); the cache is
+ * written before attention reads it, with K already rotated by RoPE
+ * (ADR-0060 GQA fused attention, §0.5.1 and §2.1).
+ *
+ *  k_new, v_new [n_new_rows, H_kv, d] storage dtype: branch b's
+ *             branch_n_new(b) rows contiguous, branches in order
+ *  k_pages    [n_pages, H_kv, page_size, d]  the pool, written in place
+ *  v_pages
+ *  page_table [n_branches, max_pages_per_branch] int32 physical page ids
+ *  branch_private_len (host) [n_branches]: private tokens each branch has
+ *             before the call; branch_n_new (host) [n_branches]: rows added
+ *  stream     hipStream_t (NULL = default stream)
+ *
+ * Row i of branch b becomes private token p = private_len(b) + i, stored at
+ * page page_table[b][p / page_size], slot p % page_size; the copy is
+ * bit-exact. private_len(b) + n_new(b) must fit the branch's table row. A
+ * page id outside [0, n_pages) is a broken precondition: that row is not
+ * written. Stream-ordered and asynchronous like gqa_attn_forward; the
+ * per-row list is uploaded only when (private_len, n_new) differ from the
+ * previous call's. Errors:
+ * GQA_ERR_INVALID_ARG, GQA_ERR_NO_MEMORY (growth of the handle's row list),
+ * GQA_ERR_HIP. */
+gqa_status gqa_attn_append_kv(gqa_attn* h, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                              int32_t n_pages, const int32_t* page_table, int32_t max_pages_per_branch,
+                              int32_t n_branches, const int32_t* branch_private_len,
+                              const int32_t* branch_n_new, void* stream);
+
 /* Release the handle (waits for its outstanding work). NULL is accepted. */
 gqa_status gqa_attn_destroy(gqa_attn* h);
 
@@ -177,6 +207,11 @@ gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n);
 gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable);
 gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
                                  int64_t* n_forwards);
+
+/* Kernel time of the appends made while timing is enabled (events that each
+ * append launch records around its own kernel, like gqa_attn_kernel_times):
+ * summed milliseconds and the number of appends, then cleared. */
+gqa_status gqa_attn_append_times(gqa_attn* h, double* ms, int64_t* n_calls);
 
 /* Host-only planner check (no device use): plans the given metadata with
  * the handle-free parameters `p` for a 256-CU device with one resident

@@ -81,6 +81,30 @@ def private_location(i: int, page_size: int) -> Tuple[int, int]:
     return i // page_size, i % page_size
 
 
+def append_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
+              private_len: Sequence[int], n_new: Sequence[int], k_new: torch.Tensor, v_new: torch.Tensor,
+              page_size: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The page pools after appending new rows to each branch's private
+    suffix (AHBM Agentic Runtime Architecture, §3.1: a branch's tokens go to
+    its own pages, slot after slot; ADR-0060 GQA fused attention, §0.5.1: the
+    cache is written before attention reads it). k_new / v_new hold branch
+    b's n_new[b] rows ([rows, H_kv, d]) contiguously, branches in order; row
+    i of branch b becomes private token private_len[b] + i. Returns CPU
+    copies of the pools; the inputs are left as they are."""
+    kp, vp = k_pages.to("cpu").clone(), v_pages.to("cpu").clone()
+    kn, vn = k_new.to("cpu"), v_new.to("cpu")
+    table = page_table.to("cpu").tolist()
+    r = 0
+    for b in range(len(n_new)):
+        for i in range(n_new[b]):
+            lp, slot = private_location(private_len[b] + i, page_size)
+            page = table[b][lp]
+            kp[page, :, slot, :] = kn[r]
+            vp[page, :, slot, :] = vn[r]
+            r += 1
+    return kp, vp
+
+
 # ----------------------------------------------------------------- context --
 def branch_context(inp, b: int, page_size: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """K_b, V_b as float64 [C_b, H_kv, d]: the group's shared prefix followed

@@ -412,12 +412,64 @@ def pin_invariant_paging():
     assert torch.equal(o3, o) and torch.equal(l3, lse)
 
 
+def pin_golden_append_placement():
+    """Appended rows land where the paging rule puts them, worked by hand:
+    4-token pages; branch 0 holds 3 private tokens in pages [5, 2, 7] and
+    gets 4 more, so they fill slot 3 of page 5 and slots 0..2 of page 2;
+    branch 1 holds none in pages [1, 6] and gets 2, slots 0 and 1 of page 1.
+    Nothing else in the pool changes."""
+    ps, n_pages = 4, 8
+    k_pages = torch.arange(n_pages * 1 * ps * 2, dtype=torch.float32).view(n_pages, 1, ps, 2) * -1.0
+    v_pages = k_pages - 1000.0
+    table = torch.tensor([[5, 2, 7], [1, 6, -1]], dtype=torch.int32)
+    k_new = torch.tensor([[[10.0, 11.0]], [[20.0, 21.0]], [[30.0, 31.0]], [[40.0, 41.0]],
+                          [[50.0, 51.0]], [[60.0, 61.0]]])
+    v_new = k_new + 0.5
+    kp, vp = oracle.append_kv(k_pages, v_pages, table, [3, 0], [4, 2], k_new, v_new, ps)
+    expected = {(5, 3): 0, (2, 0): 1, (2, 1): 2, (2, 2): 3, (1, 0): 4, (1, 1): 5}
+    for page in range(n_pages):
+        for slot in range(ps):
+            if (page, slot) in expected:
+                r = expected[(page, slot)]
+                assert torch.equal(kp[page, :, slot], k_new[r]) and torch.equal(vp[page, :, slot], v_new[r])
+            else:
+                assert torch.equal(kp[page, :, slot], k_pages[page, :, slot])
+                assert torch.equal(vp[page, :, slot], v_pages[page, :, slot])
+
+
+def pin_invariant_append_then_attend():
+    """Attention after appending a branch's last rows to a pool that lacked
+    them equals attention over the pool that held them from the start."""
+    w = custom("append", H_q=4, H_kv=2, d=16, page_size=4, shared=(10,),
+               branches=((0, 3, 11), (0, 2, 6)), seed=31)
+    inp = generate(w, "cpu")
+    o, lse = run_oracle(w, inp)
+    n_new = [5, 2]
+    keep = [L - n for L, n in zip(inp.branch_private_len, n_new)]
+    ks, vs, kp, vp = [], [], inp.k_pages.clone(), inp.v_pages.clone()
+    for b, (k0, n) in enumerate(zip(keep, n_new)):
+        walk_k, walk_v = context_by_walk(inp, b, w.page_size)
+        C = len(walk_k)
+        for i in range(n):
+            ks.append(torch.tensor(walk_k[C - n + i], dtype=inp.k_pages.dtype))
+            vs.append(torch.tensor(walk_v[C - n + i], dtype=inp.v_pages.dtype))
+            page = int(inp.page_table[b][(k0 + i) // w.page_size])
+            kp[page, :, (k0 + i) % w.page_size] = 0
+            vp[page, :, (k0 + i) % w.page_size] = 0
+    kp, vp = oracle.append_kv(kp, vp, inp.page_table, keep, n_new, torch.stack(ks), torch.stack(vs), w.page_size)
+    inp2 = Inputs(inp.q, inp.k_shared, inp.v_shared, kp, vp, inp.page_table, inp.group_shared_start,
+                  inp.group_shared_len, inp.branch_group, inp.branch_q_len, inp.branch_private_len)
+    o2, l2 = run_oracle(w, inp2)
+    assert torch.equal(o2, o) and torch.equal(l2, lse)
+
+
 ALL_PINS = [
     pin_golden_weights_123, pin_golden_paged_causal, pin_golden_merge,
     pin_brute_force_tiny, pin_library_sdpa, pin_closed_form_zero_q,
     pin_closed_form_prefill_row0, pin_closed_form_dominant_key,
     pin_invariant_batching, pin_invariant_split_merge, pin_invariant_causal,
-    pin_invariant_gqa_map, pin_invariant_paging,
+    pin_invariant_gqa_map, pin_invariant_paging, pin_golden_append_placement,
+    pin_invariant_append_then_attend,
 ]
 
 

@@ -36,6 +36,11 @@ def _branch_context_swapped(inp, b, page_size):
 
 
 ORIGINAL_BRANCH_CONTEXT = OA.branch_context
+ORIGINAL_APPEND = OA.append_kv
+
+
+def _append_from_front(k_pages, v_pages, table, private_len, n_new, k_new, v_new, ps):
+    return ORIGINAL_APPEND(k_pages, v_pages, table, [0] * len(n_new), n_new, k_new, v_new, ps)
 
 MUTATIONS = {
     "gqa_interleaved_heads": ("kv_head_of", lambda h, hq, hkv: h % hkv),
@@ -53,6 +58,7 @@ MUTATIONS = {
     "lse_log2": ("lse_of", lambda m, l: m + torch.log2(l)),
     "merge_drops_rescale": ("merge_states", _merge_drop_b_scale),
     "k_and_v_swapped": ("branch_context", _branch_context_swapped),
+    "append_from_slot_zero": ("append_kv", _append_from_front),
 }
 
 
