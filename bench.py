@@ -35,6 +35,7 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 matrix/vector (published)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E (published)
 LLC_BYTES = 256 << 20           # Infinity Cache
+CLOCK_WARMUP_S = 0.3            # untimed sustained load before each timed region
 
 WORKLOADS = {"fanout": "fanout_8x20_32k", "decode": "decode_8k", "prefill": "prefill_32k",
              "mixed": "mixed_32dec_64x4", "tiny": "tiny_fp32_fanout", "join400": "join_400_32k",
@@ -72,41 +73,71 @@ def clone_inputs(inp, n):
     return out
 
 
-def run_workload(name: str, steps: int, warmup: int, log):
-    """Times `steps` forwards of the named workload; returns (workload, result dict)."""
+class Prepared:
+    """A workload's inputs on the device: enough rotated copies that the K/V
+    working set is at least twice the Infinity Cache (a rotation just above
+    its size still hits in it for a good part), so every step reads its K/V
+    from HBM."""
+
+    def __init__(self, name, log):
+        import torch
+
+        from workload import generate, get_workload
+
+        self.w = w = get_workload(name) if isinstance(name, str) else name
+        t0 = time.time()
+        base = generate(w, "cuda")
+        n_copies = max(1, min(16, -(-2 * LLC_BYTES // max(1, w.kv_bytes()))))
+        if w.kv_bytes() > 4 * LLC_BYTES:
+            n_copies = 1
+        self.copies = clone_inputs(base, n_copies)
+        self.out = torch.empty_like(base.q)
+        self.lse = torch.empty(base.q.shape[0], w.num_q_heads, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] {w.name}: inputs ready ({n_copies} copies, {time.time() - t0:.1f}s)")
+
+    def close(self):
+        import torch
+        del self.copies, self.out, self.lse
+        torch.cuda.empty_cache()
+
+
+def time_forwards(p: Prepared, steps: int, warmup: int, log, splits="config"):
+    """Times `steps` forwards of a prepared workload; returns the result dict.
+    splits: "config" uses the workload's own split list (None: heuristic);
+    a list overrides it (one entry per unit, 0 = heuristic)."""
     import torch
 
     import gqa_attention_agentic_amd as G
-    from workload import generate, get_workload
 
-    w = get_workload(name)
-    t0 = time.time()
-    base = generate(w, "cuda")
-    kv_bytes = w.kv_bytes()
-    # Rotate enough input copies that the working set is at least twice the
-    # Infinity Cache (a rotation just above its size still hits in it for a
-    # good part): every step then reads its K/V from HBM.
-    n_copies = max(1, min(16, -(-2 * LLC_BYTES // max(1, kv_bytes))))
-    if kv_bytes > 4 * LLC_BYTES:
-        n_copies = 1
-    copies = clone_inputs(base, n_copies)
-    torch.cuda.synchronize()
-    log(f"[bench] {w.name}: inputs ready ({n_copies} copies, {time.time() - t0:.1f}s)")
+    w, copies = p.w, p.copies
+    n_copies = len(copies)
+    split_list = w.splits if isinstance(splits, str) else splits
     h = G.GqaAttention(w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, w.dtype)
-    out = torch.empty_like(base.q)
-    lse = torch.empty(base.q.shape[0], w.num_q_heads, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i):
-        h.forward_inputs(copies[i % n_copies], w.causal, splits=w.splits, out=out, lse=lse,
+        h.forward_inputs(copies[i % n_copies], w.causal, splits=split_list, out=p.out, lse=p.lse,
                          stream=stream.cuda_stream)
 
     # Every input copy is used once before timing, so no timed step pays a
-    # first touch (page-table walks) of a copy.
+    # first touch (page-table walks) of a copy. The warm-up then goes on
+    # until the GPU has been kept busy for CLOCK_WARMUP_S: it leaves its
+    # low-power clocks only after some tens of milliseconds of sustained load
+    # (measured on MI355X: the fan-out's attention launch takes ~220 us in
+    # the first ~10 ms of load and ~183 us after ~50 ms).
     warmup = max(warmup, n_copies)
+    t0 = time.perf_counter()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    per_step = max(1e-6, (time.perf_counter() - t0) / warmup)
+    batch = max(1, int(0.02 / per_step))   # ~20 ms of work between host checks
+    while time.perf_counter() - t0 < CLOCK_WARMUP_S:
+        for _ in range(batch):
+            step(warmup)
+            warmup += 1
+        torch.cuda.synchronize()
     h.enable_timing(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -121,7 +152,7 @@ def run_workload(name: str, steps: int, warmup: int, log):
     attn_ms /= max(1, n)
     merge_ms /= max(1, n)
     stats = h.plan_stats()
-    flops = w.flops()
+    flops, kv_bytes = w.flops(), w.kv_bytes()
     res = {
         "workload": w.name,
         "description": w.description,
@@ -143,9 +174,15 @@ def run_workload(name: str, steps: int, warmup: int, log):
     log(f"[bench] {w.name}: {wall_ms:.4f} ms/step, attention {attn_ms:.4f} ms, merge {merge_ms:.4f} ms, "
         f"{res['tflops']:.1f} TFLOP/s, KV {res['kv_gbps']:.0f} GB/s")
     h.close()
-    del copies, base
-    torch.cuda.empty_cache()
-    return w, res
+    return res
+
+
+def run_workload(name: str, steps: int, warmup: int, log):
+    """Times `steps` forwards of the named workload; returns (workload, result dict)."""
+    p = Prepared(name, log)
+    res = time_forwards(p, steps, warmup, log)
+    p.close()
+    return p.w, res
 
 
 def run_append(steps: int, warmup: int, log):
@@ -180,9 +217,13 @@ def run_append(steps: int, warmup: int, log):
         kn, vn, kp, vp, table = sets[i % n_copies]
         h.append_kv(kn, vn, kp, vp, table, [0], [rows], stream=stream.cuda_stream)
 
-    for i in range(max(warmup, n_copies)):
-        step(i)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < max(warmup, n_copies) or time.perf_counter() - t0 < CLOCK_WARMUP_S:
+        for _ in range(64):
+            step(n_warm)
+            n_warm += 1
+        torch.cuda.synchronize()
     h.enable_timing(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -277,6 +318,134 @@ def cpu_baseline(name: str, budget_s: float, log):
             "sample": sample, "cpu": cpu_model(), "os_cpu_count": os.cpu_count(), "seconds": spent}
 
 
+# Split counts swept for the first unit (the group's shared prefix) of each
+# workload; the other units keep the library's heuristic (0).
+SWEEPS = {"decode": [1, 2, 4, 8, 16, 24, 32, 48, 64, 128],
+          "fanout": [1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16],
+          "prefill": [1, 2, 4, 8, 16],
+          "join400": [1, 2, 4, 6, 7, 8, 12, 16]}
+
+
+def sweep_splits(name: str, steps: int, warmup: int, log, out_path: str):
+    """Times the workload at each swept split count of its shared prefix and
+    with every unit left to the heuristic; prints a table and writes the
+    points (with the number of forwards each issued, for grouping a kernel
+    trace of the same run) to out_path."""
+    p = Prepared(WORKLOADS[name], log)
+    n_units = len(p.w.groups) + len(p.w.branches)
+    points = [("heuristic", [0] * n_units)] + [(str(k), [k] + [0] * (n_units - 1)) for k in SWEEPS[name]]
+    if p.w.splits is not None:
+        points.insert(1, ("workload's own", list(p.w.splits)))
+    rows = []
+    for label, sp in points:
+        r = time_forwards(p, steps, warmup, log, splits=sp)
+        rows.append({"label": label, "splits_override": sp, "chosen": r["splits"][:2],
+                     "forwards": r["warmup_steps"] + steps, "timed": steps,
+                     "attn_us": r["attn_kernel_ms"] * 1e3, "merge_us": r["merge_kernel_ms"] * 1e3,
+                     "wall_us": r["ms_per_step"] * 1e3, "plan": r["plan"]})
+    p.close()
+    print(f"split sweep of {p.w.name} ({p.w.description}); kernel times from the library's HIP events, "
+          f"mean over {steps} timed forwards")
+    print("| point | splits (prefix, first suffix) | items wide / narrow | merge launch | attention us | merge us | wall us |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        pl = r["plan"]
+        print(f"| {r['label']} | {r['chosen'][0]}, {r['chosen'][1]} | {pl['n_items_wide']} / {pl['n_items_narrow']} | "
+              f"{pl['merge_launch']} | {r['attn_us']:.1f} | {r['merge_us']:.1f} | {r['wall_us']:.1f} |")
+    with open(out_path, "w") as f:
+        json.dump({"workload": p.w.name, "points": rows}, f, indent=1)
+
+
+def read_kernel_trace(csv_path: str):
+    """(kernel name, start ns, end ns) of every dispatch in a rocprofv3
+    kernel-trace CSV, in start order."""
+    import csv
+
+    out = []
+    with open(csv_path) as f:
+        for rec in csv.DictReader(f):
+            out.append((rec.get("Kernel_Name", ""), int(rec["Start_Timestamp"]), int(rec["End_Timestamp"])))
+    out.sort(key=lambda x: x[1])
+    return out
+
+
+def kernel_summary(csv_path: str, last: int):
+    """Per-kernel durations of a bench run's kernel trace: all calls, and the
+    last `last` calls (the timed steps of a single-workload run)."""
+    import statistics
+
+    by = {}
+    for name, s, e in read_kernel_trace(csv_path):
+        by.setdefault(name, []).append((e - s) / 1e3)
+    print(f"| kernel | calls | average us (all calls) | average us (last {last} calls) | median us (last {last}) | min us |")
+    print("|---|---|---|---|---|---|")
+    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        tail = d[-last:]
+        print(f"| {name} | {len(d)} | {sum(d) / len(d):.2f} | {sum(tail) / len(tail):.2f} | "
+              f"{statistics.median(tail):.2f} | {min(d):.2f} |")
+
+
+def counter_summary(csv_path: str, last: int):
+    """Per-kernel means of a rocprofv3 --pmc CSV (one row per dispatch and
+    counter) over each kernel's last `last` dispatches, with the dispatch
+    duration and each counter's rate per nanosecond of it."""
+    import csv
+
+    rows = {}
+    with open(csv_path) as f:
+        for rec in csv.DictReader(f):
+            key = (rec["Kernel_Name"], int(rec["Dispatch_Id"]))
+            d = rows.setdefault(key, {"dur": int(rec["End_Timestamp"]) - int(rec["Start_Timestamp"])})
+            d[rec["Counter_Name"]] = d.get(rec["Counter_Name"], 0.0) + float(rec["Counter_Value"])
+    by = {}
+    for (name, disp), d in sorted(rows.items(), key=lambda kv: kv[0][1]):
+        by.setdefault(name, []).append(d)
+    for name, ds in by.items():
+        tail = ds[-last:]
+        cols = sorted(k for k in tail[0] if k != "dur")
+        dur = sum(d["dur"] for d in tail) / len(tail)
+        print(f"{name}: {len(ds)} dispatches, mean over the last {len(tail)}: duration {dur / 1e3:.2f} us")
+        for c in cols:
+            v = sum(d.get(c, 0.0) for d in tail) / len(tail)
+            print(f"  {c} = {v:.6g} ({v / dur:.4g} per ns)")
+
+
+def trace_summary(sweep_path: str, csv_path: str):
+    """Per-point kernel durations from a rocprofv3 kernel-trace CSV of a
+    sweep run: dispatches of the attention and merge kernels, in start order,
+    are assigned to the sweep points by the number of forwards each point
+    issued; each point's average covers its timed forwards only."""
+    with open(sweep_path) as f:
+        sweep = json.load(f)
+    attn, merge = [], []
+    for name, s, e in read_kernel_trace(csv_path):
+        if "attn_" in name:
+            attn.append((s, e))
+        elif "lse_merge" in name:
+            merge.append((s, e))
+    ia = im = 0
+    print(f"| point | attention launches | attention us (rocprofv3, timed forwards) | merge us | library events: attention / merge us |")
+    print("|---|---|---|---|---|")
+    for r in sweep["points"]:
+        pl = r["plan"]
+        per_fwd = int(pl["n_items_wide"] > 0) + int(pl["n_items_narrow"] > 0)
+        n = r["forwards"]
+        a = attn[ia:ia + per_fwd * n]
+        ia += per_fwd * n
+        spans = [max(e for _, e in a[k:k + per_fwd]) - min(s for s, _ in a[k:k + per_fwd])
+                 for k in range(0, len(a), per_fwd)][-r["timed"]:]
+        m_us = 0.0
+        if pl["merge_launch"]:
+            m = merge[im:im + n]
+            im += n
+            m_us = sum(e - s for s, e in m[-r["timed"]:]) / max(1, r["timed"]) / 1e3
+        a_us = sum(spans) / max(1, len(spans)) / 1e3
+        print(f"| {r['label']} ({r['chosen'][0]}) | {per_fwd} x {n} | {a_us:.1f} | {m_us:.1f} | "
+              f"{r['attn_us']:.1f} / {r['merge_us']:.1f} |")
+    if ia != len(attn) or im != len(merge):
+        print(f"(dispatch count mismatch: attention {ia} of {len(attn)}, merge {im} of {len(merge)})")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,7 +459,27 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB each, so that byte counters read "
                          "under a profiler can be scaled by a copy of known size")
+    ap.add_argument("--sweep-splits", choices=sorted(SWEEPS), default=None,
+                    help="time the workload over a range of split counts instead of the bench line")
+    ap.add_argument("--sweep-out", default="gpurun_out/sweep.json")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("SWEEP_JSON", "KERNEL_TRACE_CSV"), default=None,
+                    help="print per-point rocprofv3 kernel durations of a sweep run (no GPU needed)")
+    ap.add_argument("--kernel-summary", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="print per-kernel rocprofv3 durations of a bench run, the last --steps calls "
+                         "apart (no GPU needed)")
+    ap.add_argument("--counter-summary", metavar="PMC_CSV", default=None,
+                    help="print per-kernel means of a rocprofv3 --pmc run over the last --steps dispatches "
+                         "(no GPU needed)")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
+    if args.kernel_summary:
+        kernel_summary(args.kernel_summary, args.steps)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.steps)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -315,6 +504,10 @@ def main():
         log(f"[bench] calibration: 3 device copies of {n} bytes")
         del src, dst
 
+    if args.sweep_splits:
+        os.makedirs(os.path.dirname(os.path.abspath(args.sweep_out)), exist_ok=True)
+        sweep_splits(args.sweep_splits, args.steps, args.warmup, log, args.sweep_out)
+        return
     w, res = run_workload(WORKLOADS[args.workload], args.steps, args.warmup, log)
     traffic = traffic_for(w)
     others = {}
@@ -354,6 +547,7 @@ def main():
         "splits": res["splits"],
         "input_copies": res["input_copies"],
         "warmup_steps": res["warmup_steps"],
+        "clock_warmup_s": CLOCK_WARMUP_S,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget, log)

@@ -348,10 +348,18 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     return in.splits_override.empty() ? 0 : in.splits_override[api_slot[ui]];
   };
   // KV-bandwidth-bound units (<= 32 rows, decode-like): cut the total KV
-  // stream into about one item per resident workgroup slot, no shard below
-  // 256 keys, so every slot streams a similar number of bytes (ADR-0060,
-  // §5.2-§5.3: decode is bound by KV loads).
-  const int64_t slots = 2LL * std::max(1, in.narrow_per_cu) * P->narrow_cus;   // about two items per resident workgroup
+  // stream into about one item per resident workgroup, no shard below 256
+  // keys, so every workgroup streams a similar number of bytes once
+  // (ADR-0060, §5.2-§5.3: decode is bound by KV loads). A workgroup runs its
+  // items one after another, each paying a full memory latency and its
+  // partial write, so a second item per workgroup costs more than the finer
+  // balance gains (measured on MI355X: one 16k-token decode 37.6 us at two
+  // items per workgroup, 24.7 us at one; four 8k-token decodes 48.1 us
+  // against 34.5 us).
+#ifndef GQA_NARROW_ITEMS_PER_WG
+#define GQA_NARROW_ITEMS_PER_WG 1
+#endif
+  const int64_t slots = (int64_t)GQA_NARROW_ITEMS_PER_WG * std::max(1, in.narrow_per_cu) * P->narrow_cus;
   const int64_t wide_slots = (int64_t)std::max(1, in.wide_per_cu) * P->wide_cus;
   {
     int64_t wn = 0;

@@ -162,6 +162,24 @@ def test_heuristic_fills_the_device():
     assert all(s >= 1 for s in splits[1:])
 
 
+@pytest.mark.parametrize("n,L", [(1, 16384), (1, 65536), (4, 8192), (16, 2048), (1, 2048)])
+def test_decode_heuristic_one_item_per_workgroup(n, L):
+    """Decode-like units (<= 32 rows) are cut into about one item per
+    resident workgroup (256 on the host planner's 256 CUs), never below 256
+    keys per shard, with equal shard counts for equal lengths; a second item
+    per workgroup would queue a second full memory latency behind the first."""
+    from workload.configs import Branch, Group, _llama
+
+    w = _llama("d", [Group(0)], [Branch(0, 1, L) for _ in range(n)], causal=True, seed=2)
+    items, splits, stats = _plan(w, splits=None)
+    narrow = [it for it in items if it[7] == 1]
+    assert stats["n_items_wide"] == 0
+    assert len(narrow) <= 256 and len(narrow) >= min(256, n * 8 * (L // 256)) // 2, len(narrow)
+    assert len(set(splits[1:])) == 1
+    assert all(it[5] - it[4] >= 256 or it[5] == L for it in narrow)
+    assert max(it[8] for it in narrow) + 1 == len(narrow)      # one item per workgroup
+
+
 def _item_cost(it):
     return it[5] - it[4] + 96       # keys plus the planner's fixed per-item cost
 
