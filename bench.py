@@ -410,6 +410,55 @@ def counter_summary(csv_path: str, last: int):
             print(f"  {c} = {v:.6g} ({v / dur:.4g} per ns)")
 
 
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, last: int, cmd_fetch: str, cmd_write: str):
+    """HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) of `bench.py --copy-calibration 1024`:
+    each counter is scaled by 2^30 bytes over what it read for the largest
+    plain device copy (2^30 bytes) of the same run, then averaged over each
+    attention / merge kernel's last `last` dispatches. Writes
+    profiles/traffic_<workload>.json."""
+    import csv
+
+    from workload import get_workload
+
+    def read(path, counter):
+        per = {}
+        with open(path) as f:
+            for rec in csv.DictReader(f):
+                if rec["Counter_Name"] != counter:
+                    continue
+                key = (int(rec["Dispatch_Id"]), rec["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(rec["Counter_Value"])
+        rows = [(d, n, v) for (d, n), v in sorted(per.items())]
+        copy = max(v for _, n, v in rows if "gqa::" not in n)
+        scale = (1 << 30) / (copy * 1024.0)
+        by = {}
+        for _, n, v in rows:
+            if "gqa::" in n:
+                by.setdefault(n, []).append(v)
+        return scale, {n: sum(v[-last:]) / len(v[-last:]) * 1024.0 * scale for n, v in by.items()}
+
+    fs, fetch = read(fetch_csv, "FETCH_SIZE")
+    ws, write = read(write_csv, "WRITE_SIZE")
+    short = lambda n: n.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
+    per_kernel = {short(n): {"fetch_bytes": round(fetch[n]), "write_bytes": round(write.get(n, 0.0))} for n in fetch}
+    attn = [k for k in per_kernel if k.startswith("attn_")]
+    w = get_workload(WORKLOADS[workload])
+    out = {"workload": w.name, "kernel_hash": kernel_hash(),
+           "hbm_bytes_per_launch": sum(per_kernel[k]["fetch_bytes"] + per_kernel[k]["write_bytes"] for k in attn),
+           "per_kernel": per_kernel, "fetch_scale": fs, "write_scale": ws,
+           "calibration": f"FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by 2^30 bytes / the counter read "
+                          f"for a device copy of 2^30 bytes in the same run (fetch x{fs:.4f}, write x{ws:.4f})",
+           "algorithmic_bytes": w.kv_bytes() + w.io_bytes(),
+           "command_fetch": cmd_fetch, "command_write": cmd_write}
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    for k, v in per_kernel.items():
+        print(f"| {k} | {v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |")
+    print(f"wrote {path}")
+
+
 def trace_summary(sweep_path: str, csv_path: str):
     """Per-point kernel durations from a rocprofv3 kernel-trace CSV of a
     sweep run: dispatches of the attention and merge kernels, in start order,
@@ -470,6 +519,9 @@ def main():
     ap.add_argument("--counter-summary", metavar="PMC_CSV", default=None,
                     help="print per-kernel means of a rocprofv3 --pmc run over the last --steps dispatches "
                          "(no GPU needed)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
+                    default=None, help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs "
+                                       "of --workload (no GPU needed)")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(*args.trace_summary)
@@ -479,6 +531,9 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, args.steps)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary[:2], args.workload, args.steps, *args.traffic_summary[2:])
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
