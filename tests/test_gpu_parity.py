@@ -63,6 +63,30 @@ SMALL = {
     "single_key": lambda: custom("single_key", shared=(1,), branches=((0, 1, 0),), seed=116),
     "join_continuation": lambda: custom("join_continuation", shared=(700,), branches=((0, 60, 60),),
                                         seed=118),
+    # The largest query-head group one M-tile holds: 256 heads of one token
+    # per KV head (bf16), 128 (fp32).
+    "max_group_bf16": lambda: custom("max_group_bf16", H_q=256, H_kv=1, d=64, shared=(150,),
+                                     branches=((0, 2, 30), (0, 3, 17)), seed=120),
+    "max_group_fp32": lambda: custom("max_group_fp32", dtype="fp32", H_q=128, H_kv=1, d=64, page_size=8,
+                                     shared=(90,), branches=((0, 2, 10),), seed=121),
+    # Degenerate and large pages: one token per page, and a page far longer
+    # than the suffix's tail.
+    "page_size_1": lambda: custom("page_size_1", page_size=1, shared=(64,), branches=((0, 3, 9), (0, 2, 5)),
+                                  seed=122),
+    "page_size_512": lambda: custom("page_size_512", page_size=512, shared=(100,), branches=((0, 4, 700),),
+                                    seed=123),
+    # Forty one-token branches over one prefix: many tokens per narrow
+    # M-tile, each combined inside the narrow launch.
+    "many_branch_decode": lambda: custom("many_branch_decode", shared=(400,),
+                                         branches=tuple((0, 1, k) for k in range(40)), seed=124),
+    # Independent paged decodes of very different lengths (the split
+    # heuristic gives each about one item per workgroup).
+    "batched_paged_decodes": lambda: custom("batched_paged_decodes", shared=(0,),
+                                            branches=((0, 1, 3000), (0, 1, 1200), (0, 1, 5000), (0, 1, 17)),
+                                            seed=125),
+    # Non-causal multi-token queries: every key of the context is visible.
+    "noncausal_fanout": lambda: custom("noncausal_fanout", shared=(300,), branches=((0, 5, 40), (0, 7, 21)),
+                                       causal=False, seed=126),
 }
 
 
