@@ -10,11 +10,20 @@ Llama3-70B heads: H_q 64, H_kv 8, d 128, bf16). Input copies are rotated so
 the K/V working set is at least twice the 256 MB last-level cache and every
 step reads its K/V from HBM.
 
+Before each timed region the forward runs untimed until the GPU has been
+busy for CLOCK_WARMUP_S (the clocks leave their low-power state only under
+sustained load); the timed region is exactly K forwards.
+
 Prints ONE JSON line: throughput (TFLOP/s on the algorithmic FLOP count),
 effective KV GB/s, the roofline of the dominant kernel (timed with HIP
 events recorded by the library on the forward's stream), the fp64 CPU oracle
 timed on a bounded sample on this host, and secondary lines for the other
-workloads (decode, prefill, mixed).
+workloads (decode, prefill, mixed, joins, K/V append).
+
+Other modes: --sweep-splits W times a workload over a range of shard counts
+(GPU); --kernel-summary, --counter-summary, --trace-summary and
+--traffic-summary turn rocprofv3 output into the tables under profiles/ (no
+GPU needed).
 """
 
 from __future__ import annotations
@@ -41,11 +50,12 @@ WORKLOADS = {"fanout": "fanout_8x20_32k", "decode": "decode_8k", "prefill": "pre
              "mixed": "mixed_32dec_64x4", "tiny": "tiny_fp32_fanout", "join400": "join_400_32k",
              "join8000": "join_8000_32k"}
 KERNEL_SOURCES = ["gqa_attention_agentic_amd/csrc/attention.hip"]
+APPEND_SOURCES = ["gqa_attention_agentic_amd/csrc/append.hip"]
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -237,10 +247,20 @@ def run_append(steps: int, warmup: int, log):
     kms /= max(1, n)
     gbps = moved / (kms * 1e-3) / 1e9
     log(f"[bench] append 8000 rows: {ms * 1e3:.1f} us/call wall, kernel {kms * 1e3:.1f} us, {gbps:.0f} GB/s")
+    # HBM bytes of the append kernel from the counter runs that profiled it
+    # (a decode run with the append leg), while its source is unchanged.
+    traffic = None
+    path = os.path.join(ROOT, "profiles", "traffic_decode_8k.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            t = json.load(f)
+        a = t.get("per_kernel", {}).get("append_kv_rows")
+        if a and t.get("append_kernel_hash") == kernel_hash(APPEND_SOURCES):
+            traffic = a["fetch_bytes"] + a["write_bytes"]
     return {"workload": "append_kv: 8000 rows (join input) into 16-token pages", "ms_per_step": ms,
             "kernel_ms": kms, "bytes_per_call": moved, "input_copies": n_copies,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": gbps / PEAK_HBM_GBPS, "traffic": None}}
+                         "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic}}
 
 
 def roofline_of(w, res, traffic):
@@ -451,6 +471,8 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, last: int, cm
                           f"for a device copy of 2^30 bytes in the same run (fetch x{fs:.4f}, write x{ws:.4f})",
            "algorithmic_bytes": w.kv_bytes() + w.io_bytes(),
            "command_fetch": cmd_fetch, "command_write": cmd_write}
+    if "append_kv_rows" in per_kernel:
+        out["append_kernel_hash"] = kernel_hash(APPEND_SOURCES)
     path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
