@@ -16,6 +16,7 @@ from workload import custom, generate, get_workload
 from workload.generate import Inputs
 
 import gpu_helpers as H
+import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -297,3 +298,44 @@ def test_join_8000_32k_sampled():
     rng = random.Random(7)
     toks = {0, 1, 31, 32, 63, 64, 4095, 4096, 7999} | {rng.randrange(8000) for _ in range(3)}
     _sample_parity("join_8000_32k", [0], sorted(toks))
+
+
+def _passes(w, o, lse, o_ref, l_ref, toks, label):
+    try:
+        H.compare(w, o, lse, o_ref, l_ref, toks, label=label)
+        return True
+    except AssertionError:
+        return False
+
+
+def test_parity_check_rejects_planted_mistakes():
+    """Mutation sanity on peaked scores: the library's output passes against
+    the oracle, and fails against the oracle run on CPU inputs with a planted
+    mistake -- the first third of the shared prefix (a shard) dropped, the
+    private suffixes skipped, or two pages of a branch swapped."""
+    w = SMALL["peaked_fanout"]()
+    inp = generate(w, "cuda")
+    o, lse, _ = H.run_library(w, inp)
+    sub, toks = H.cpu_subset(inp, range(len(inp.branch_q_len)))
+
+    def ref(x):
+        return oracle.attention(x, w.num_kv_heads, w.page_size, w.causal)
+
+    o_ref, l_ref = ref(sub)
+    assert _passes(w, o, lse, o_ref, l_ref, toks, "correct oracle")
+    L = sub.group_shared_len[0]
+    a = L // 3
+    dropped = Inputs(sub.q, sub.k_shared[:, a:].contiguous(), sub.v_shared[:, a:].contiguous(), sub.k_pages,
+                     sub.v_pages, sub.page_table, [0], [L - a], sub.branch_group, sub.branch_q_len,
+                     sub.branch_private_len)
+    no_suffix = Inputs(sub.q, sub.k_shared, sub.v_shared, sub.k_pages, sub.v_pages, sub.page_table,
+                       sub.group_shared_start, sub.group_shared_len, sub.branch_group, sub.branch_q_len,
+                       [0] * len(sub.branch_private_len))
+    table = sub.page_table.clone()
+    table[0, 1], table[0, 2] = sub.page_table[0, 2], sub.page_table[0, 1]
+    swapped = Inputs(sub.q, sub.k_shared, sub.v_shared, sub.k_pages, sub.v_pages, table,
+                     sub.group_shared_start, sub.group_shared_len, sub.branch_group, sub.branch_q_len,
+                     sub.branch_private_len)
+    for label, x in (("shard dropped", dropped), ("suffix skipped", no_suffix), ("pages swapped", swapped)):
+        o_bad, l_bad = ref(x)
+        assert not _passes(w, o, lse, o_bad, l_bad, toks, label), f"planted mistake '{label}' passed"
