@@ -481,6 +481,83 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, last: int, cm
     print(f"wrote {path}")
 
 
+def read_once_variants():
+    """Fan-out variants over the 32768-token shared prefix (20 new tokens and
+    512 private tokens per agent, 16-token pages, H_kv 8, d 128, bf16): the
+    agent count at G = 8, then the query heads per KV head at 8 agents. The
+    prefix is stored once; every variant should fetch about its unique bytes."""
+    from workload.configs import Branch, Group, Workload
+
+    out = []
+    for n in (1, 2, 4, 8):
+        out.append((f"{n} agents, G 8", Workload(
+            name=f"fanout_{n}x20_32k", dtype="bf16", num_q_heads=64, num_kv_heads=8, head_dim=128,
+            page_size=16, groups=[Group(32768)], branches=[Branch(0, 20, 512) for _ in range(n)],
+            causal=True, seed=3, description=f"{n} agents x 20 tokens over a 32768-token prefix")))
+    for g in (1, 2, 4):
+        out.append((f"8 agents, G {g}", Workload(
+            name=f"fanout_8x20_32k_g{g}", dtype="bf16", num_q_heads=8 * g, num_kv_heads=8, head_dim=128,
+            page_size=16, groups=[Group(32768)], branches=[Branch(0, 20, 512) for _ in range(8)],
+            causal=True, seed=3, description=f"8 agents x 20 tokens, G {g}")))
+    return out
+
+
+def sweep_read_once(steps: int, warmup: int, log, out_path: str):
+    """Times each read-once variant (run it under rocprofv3 --pmc FETCH_SIZE
+    with --copy-calibration); writes the points with their forward counts
+    and unique bytes to out_path for --pmc-sweep-summary."""
+    rows = []
+    for label, w in read_once_variants():
+        p = Prepared(w, log)
+        r = time_forwards(p, steps, warmup, log, splits=None)
+        p.close()
+        rows.append({"label": label, "workload": w.name, "forwards": r["warmup_steps"] + steps, "timed": steps,
+                     "unique_bytes": w.kv_bytes() + w.io_bytes(), "kv_bytes": w.kv_bytes(),
+                     "attn_us": r["attn_kernel_ms"] * 1e3, "plan": r["plan"]})
+        print(f"{label}: attention {r['attn_kernel_ms'] * 1e3:.1f} us, unique bytes {rows[-1]['unique_bytes']:,}",
+              flush=True)
+    with open(out_path, "w") as f:
+        json.dump({"points": rows}, f, indent=1)
+
+
+def pmc_sweep_summary(sweep_path: str, csv_path: str, counter: str = "FETCH_SIZE"):
+    """Per-point HBM bytes of the attention launches of a read-once sweep run
+    under rocprofv3 --pmc: attention dispatches in dispatch order are
+    assigned to the points by their forward counts (a side-by-side forward
+    has two), each point averages its timed forwards, and KiB are scaled by
+    the largest plain device copy (2^30 bytes) of the run."""
+    import csv
+
+    with open(sweep_path) as f:
+        sweep = json.load(f)
+    per = {}
+    with open(csv_path) as f:
+        for rec in csv.DictReader(f):
+            if rec["Counter_Name"] != counter:
+                continue
+            key = (int(rec["Dispatch_Id"]), rec["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(rec["Counter_Value"])
+    rows = sorted(per.items())
+    copy = max(v for (_, n), v in rows if "gqa::" not in n)
+    scale = (1 << 30) / (copy * 1024.0)
+    attn = [v * 1024.0 * scale for (_, n), v in rows if "attn_" in n]
+    i = 0
+    print(f"| point | unique bytes (K/V once + Q, O, LSE) | {counter} of the attention launch, bytes | ratio |")
+    print("|---|---|---|---|")
+    for r in sweep["points"]:
+        pl = r["plan"]
+        per_fwd = int(pl["n_items_wide"] > 0) + int(pl["n_items_narrow"] > 0)
+        n = r["forwards"] * per_fwd
+        a = attn[i:i + n]
+        i += n
+        tail = [sum(a[k:k + per_fwd]) for k in range(0, len(a), per_fwd)][-r["timed"]:]
+        b = sum(tail) / max(1, len(tail))
+        print(f"| {r['label']} | {r['unique_bytes']:,} | {b:,.0f} | {b / r['unique_bytes']:.3f} |")
+    if i != len(attn):
+        print(f"(dispatch count mismatch: {i} of {len(attn)})")
+    print(f"(counter scale x{scale:.4f} from the largest plain copy)")
+
+
 def trace_summary(sweep_path: str, csv_path: str):
     """Per-point kernel durations from a rocprofv3 kernel-trace CSV of a
     sweep run: dispatches of the attention and merge kernels, in start order,
@@ -544,6 +621,10 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
                     default=None, help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs "
                                        "of --workload (no GPU needed)")
+    ap.add_argument("--read-once-sweep", action="store_true",
+                    help="run the fan-out at 1/2/4/8 agents and G 1/2/4/8 (for a --pmc FETCH_SIZE run)")
+    ap.add_argument("--pmc-sweep-summary", nargs=2, metavar=("SWEEP_JSON", "PMC_CSV"), default=None,
+                    help="per-point HBM bytes of a --read-once-sweep run under --pmc (no GPU needed)")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(*args.trace_summary)
@@ -553,6 +634,9 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, args.steps)
+        return
+    if args.pmc_sweep_summary:
+        pmc_sweep_summary(*args.pmc_sweep_summary)
         return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary[:2], args.workload, args.steps, *args.traffic_summary[2:])
@@ -581,6 +665,10 @@ def main():
         log(f"[bench] calibration: 3 device copies of {n} bytes")
         del src, dst
 
+    if args.read_once_sweep:
+        os.makedirs(os.path.dirname(os.path.abspath(args.sweep_out)), exist_ok=True)
+        sweep_read_once(args.steps, args.warmup, log, args.sweep_out)
+        return
     if args.sweep_splits:
         os.makedirs(os.path.dirname(os.path.abspath(args.sweep_out)), exist_ok=True)
         sweep_splits(args.sweep_splits, args.steps, args.warmup, log, args.sweep_out)
