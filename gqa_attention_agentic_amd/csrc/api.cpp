@@ -256,8 +256,12 @@ gqa_status ensure_workspace(gqa_attn* h) {
 TimerSlot* next_timer(gqa_attn* h) {
   if (h->timers_used == h->timers.size()) {
     TimerSlot t{};
-    for (auto& ev : t.ev)
-      if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+    for (int k = 0; k < 6; ++k) {
+      if (hipEventCreate(&t.ev[k]) != hipSuccess) {
+        for (int j = 0; j < k; ++j) hipEventDestroy(t.ev[j]);
+        return nullptr;   // this forward goes untimed
+      }
+    }
     h->timers.push_back(t);
   }
   return &h->timers[h->timers_used++];
@@ -397,8 +401,8 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   // token resets its counter); they are cleared here only after the plan or
   // the workspace changed.
   if (h->counters_dirty && counter_bytes(h) > 0) {
-    e = hipMemsetAsync(h->d_work, 0, counter_bytes(h), st);
-    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(counters)");
+    e = gqa::launch_zero_i32((int32_t*)h->d_work, (int64_t)(counter_bytes(h) / sizeof(int32_t)), st);
+    if (e != hipSuccess) return hip_fail(e, "counter clear");
     h->counters_dirty = false;
   }
 
@@ -462,9 +466,12 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
     a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);
     e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
                               ev(1));
+    // The caller's stream waits for the narrow kernel even when the wide
+    // launch failed, so that no later work on it overlaps a kernel still
+    // writing the outputs.
+    const hipError_t ej = hipStreamWaitEvent(st, h->join, 0);
     if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
-    e = hipStreamWaitEvent(st, h->join, 0);
-    if (e != hipSuccess) return hip_fail(e, "join from the side stream");
+    if (ej != hipSuccess) return hip_fail(ej, "join from the side stream");
   } else if (!Q.wide.empty()) {
     a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
     a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);

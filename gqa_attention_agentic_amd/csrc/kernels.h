@@ -55,6 +55,9 @@ hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_part
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 
+// Zero fill of n int32 values (fill.hip): the arrival counters.
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
+
 // Append of new K and V rows to branches' private pages (append.hip).
 struct AppendArgs {
   const void* k_new;        // [n_rows, H_kv, d]

@@ -116,7 +116,13 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out);
  * q, k/v and o must be 16-byte aligned, page_table and lse 4-byte aligned;
  * a pointer whose extent is zero may be NULL. Errors: GQA_ERR_INVALID_ARG, GQA_ERR_NO_MEMORY (workspace growth),
  * GQA_ERR_HIP (launch failure). The plan is rebuilt only when the metadata
- * differs from the previous call on this handle. */
+ * differs from the previous call on this handle. A call whose plan is cached
+ * (same metadata as the previous call, workspace already large enough)
+ * issues only kernel launches and, when its two attention kernels run side
+ * by side, the event fork / join of the handle's side stream: it allocates
+ * nothing, uploads nothing and may be captured into a HIP graph. Replays of
+ * such a graph share the handle's workspace with its other calls, so they
+ * must be ordered with them on the device. */
 gqa_status gqa_attn_forward(gqa_attn* h,
                             const void* q,
                             const void* k_shared, const void* v_shared,
