@@ -148,7 +148,9 @@ def time_forwards(p: Prepared, steps: int, warmup: int, log, splits="config"):
             step(warmup)
             warmup += 1
         torch.cuda.synchronize()
-    h.enable_timing(True)
+    # Wall clock over exactly `steps` forwards with no per-kernel events: the
+    # library's timing events cost ~9 us at every kernel boundary (measured
+    # in rocprofv3 traces: back-to-back kernels without them).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -157,6 +159,12 @@ def time_forwards(p: Prepared, steps: int, warmup: int, log, splits="config"):
     end.record(stream)
     torch.cuda.synchronize()
     wall_ms = start.elapsed_time(end) / steps
+    # Kernel durations over `steps` more forwards, from the HIP events each
+    # launch records around its own kernel on the stream it runs on.
+    h.enable_timing(True)
+    for i in range(steps):
+        step(warmup + steps + i)
+    torch.cuda.synchronize()
     attn_ms, merge_ms, n = h.kernel_times()
     h.enable_timing(False)
     attn_ms /= max(1, n)
@@ -234,7 +242,6 @@ def run_append(steps: int, warmup: int, log):
             step(n_warm)
             n_warm += 1
         torch.cuda.synchronize()
-    h.enable_timing(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
@@ -242,6 +249,10 @@ def run_append(steps: int, warmup: int, log):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    h.enable_timing(True)
+    for i in range(steps):
+        step(steps + i)
+    torch.cuda.synchronize()
     kms, n = h.append_times()
     h.enable_timing(False)
     kms /= max(1, n)
@@ -360,7 +371,7 @@ def sweep_splits(name: str, steps: int, warmup: int, log, out_path: str):
     for label, sp in points:
         r = time_forwards(p, steps, warmup, log, splits=sp)
         rows.append({"label": label, "splits_override": sp, "chosen": r["splits"][:2],
-                     "forwards": r["warmup_steps"] + steps, "timed": steps,
+                     "forwards": r["warmup_steps"] + 2 * steps, "timed": steps,
                      "attn_us": r["attn_kernel_ms"] * 1e3, "merge_us": r["merge_kernel_ms"] * 1e3,
                      "wall_us": r["ms_per_step"] * 1e3, "plan": r["plan"]})
     p.close()
@@ -511,7 +522,7 @@ def sweep_read_once(steps: int, warmup: int, log, out_path: str):
         p = Prepared(w, log)
         r = time_forwards(p, steps, warmup, log, splits=None)
         p.close()
-        rows.append({"label": label, "workload": w.name, "forwards": r["warmup_steps"] + steps, "timed": steps,
+        rows.append({"label": label, "workload": w.name, "forwards": r["warmup_steps"] + 2 * steps, "timed": steps,
                      "unique_bytes": w.kv_bytes() + w.io_bytes(), "kv_bytes": w.kv_bytes(),
                      "attn_us": r["attn_kernel_ms"] * 1e3, "plan": r["plan"]})
         print(f"{label}: attention {r['attn_kernel_ms'] * 1e3:.1f} us, unique bytes {rows[-1]['unique_bytes']:,}",
