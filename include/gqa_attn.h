@@ -209,7 +209,9 @@ gqa_status gqa_attn_plan_splits(const gqa_attn* h, int32_t* out, int32_t n);
  * and the number of forwards, then clears the records. Rows whose partials
  * all come from the narrow (decode-like) kernel are combined inside that
  * launch, so their merge time is part of attn_ms; a forward with no other
- * such rows makes no merge launch and adds 0 to merge_ms. */
+ * such rows makes no merge launch and adds 0 to merge_ms. The events are not
+ * free: on MI355X consecutive launches that record them start ~9 us apart
+ * instead of back to back, so timing is best left off outside measurement. */
 gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable);
 gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
                                  int64_t* n_forwards);
