@@ -347,25 +347,27 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   auto override_of = [&](int32_t ui) -> int32_t {
     return in.splits_override.empty() ? 0 : in.splits_override[api_slot[ui]];
   };
-  // KV-bandwidth-bound units (<= 32 rows, decode-like): cut the total KV
-  // stream into about one item per resident workgroup, no shard below 256
-  // keys, so every workgroup streams a similar number of bytes once
-  // (ADR-0060, §5.2-§5.3: decode is bound by KV loads). A workgroup runs its
-  // items one after another, each paying a full memory latency and its
-  // partial write, so a second item per workgroup costs more than the finer
-  // balance gains (measured on MI355X: one 16k-token decode 37.6 us at two
-  // items per workgroup, 24.7 us at one; four 8k-token decodes 48.1 us
-  // against 34.5 us).
-#ifndef GQA_NARROW_ITEMS_PER_WG
-#define GQA_NARROW_ITEMS_PER_WG 1
-#endif
-  const int64_t slots = (int64_t)GQA_NARROW_ITEMS_PER_WG * std::max(1, in.narrow_per_cu) * P->narrow_cus;
+  // KV-bandwidth-bound units (<= 32 rows, decode-like): cut their total K/V
+  // stream into equal-length shards (at least 256 keys), as many as give
+  // every item about 256 KiB to stream, but no fewer than half and no more
+  // than one per resident workgroup (ADR-0060, §5.2-§5.3: decode is bound by
+  // KV loads). A workgroup runs its items one after another, each paying a
+  // full memory latency and its partial write, so a second item per
+  // workgroup costs more than the finer balance gains; a short stream is
+  // bound by latency rather than bandwidth, and there fewer, longer shards
+  // leave fewer partials to combine. Measured on MI355X (one decode, H_kv 8,
+  // d 128): 8k tokens 18.2 us at 16 shards against 19.9 at 32; 2k tokens
+  // 11.6 us at 8 against 13.0 at 4; four 8k decodes 35 us at 8 shards each
+  // against 48 us at 16.
+  const int64_t slots = (int64_t)std::max(1, in.narrow_per_cu) * P->narrow_cus;
   const int64_t wide_slots = (int64_t)std::max(1, in.wide_per_cu) * P->wide_cus;
   {
     int64_t wn = 0;
     for (int32_t ui = 0; ui < nu; ++ui)
       if (P->units[ui].bm == kNarrowRows && override_of(ui) == 0) wn += (int64_t)in.H_kv * P->units[ui].key_len;
-    const int64_t chunk = std::max<int64_t>(256, ceil_div(wn, slots));
+    const int64_t bytes = wn * 2 * in.D * (in.dtype == 0 ? 2 : 4);   // K and V
+    const int64_t items = std::min(slots, std::max((slots + 1) / 2, ceil_div(bytes, 256 << 10)));
+    const int64_t chunk = std::max<int64_t>(256, ceil_div(wn, items));
     for (int32_t ui = 0; ui < nu; ++ui)
       if (P->units[ui].bm == kNarrowRows && override_of(ui) == 0)
         S[ui] = (int32_t)std::max<int64_t>(1, ceil_div(P->units[ui].key_len, chunk));

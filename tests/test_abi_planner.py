@@ -162,19 +162,21 @@ def test_heuristic_fills_the_device():
     assert all(s >= 1 for s in splits[1:])
 
 
-@pytest.mark.parametrize("n,L", [(1, 16384), (1, 65536), (4, 8192), (16, 2048), (1, 2048)])
-def test_decode_heuristic_one_item_per_workgroup(n, L):
-    """Decode-like units (<= 32 rows) are cut into about one item per
-    resident workgroup (256 on the host planner's 256 CUs), never below 256
-    keys per shard, with equal shard counts for equal lengths; a second item
-    per workgroup would queue a second full memory latency behind the first."""
+@pytest.mark.parametrize("n,L,items", [(1, 2048, 64), (1, 4096, 128), (1, 8192, 128), (1, 12288, 192),
+                                        (1, 16384, 256), (1, 65536, 256), (4, 8192, 256), (16, 2048, 256),
+                                        (2, 4096, 128)])
+def test_decode_heuristic_items(n, L, items):
+    """Decode-like units (<= 32 rows) are cut into equal shards of at least
+    256 keys, about one item per 256 KiB of K/V, but no fewer than half and
+    no more than one per resident workgroup (256 on the host planner's 256
+    CUs), and each item gets a workgroup of its own."""
     from workload.configs import Branch, Group, _llama
 
     w = _llama("d", [Group(0)], [Branch(0, 1, L) for _ in range(n)], causal=True, seed=2)
-    items, splits, stats = _plan(w, splits=None)
-    narrow = [it for it in items if it[7] == 1]
+    plan_items, splits, stats = _plan(w, splits=None)
+    narrow = [it for it in plan_items if it[7] == 1]
     assert stats["n_items_wide"] == 0
-    assert len(narrow) <= 256 and len(narrow) >= min(256, n * 8 * (L // 256)) // 2, len(narrow)
+    assert len(narrow) == items, (len(narrow), splits)
     assert len(set(splits[1:])) == 1
     assert all(it[5] - it[4] >= 256 or it[5] == L for it in narrow)
     assert max(it[8] for it in narrow) + 1 == len(narrow)      # one item per workgroup
