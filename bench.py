@@ -195,10 +195,10 @@ def time_forwards(p: Prepared, steps: int, warmup: int, log, splits="config"):
     return res
 
 
-def run_workload(name: str, steps: int, warmup: int, log):
+def run_workload(name: str, steps: int, warmup: int, log, splits="config"):
     """Times `steps` forwards of the named workload; returns (workload, result dict)."""
     p = Prepared(name, log)
-    res = time_forwards(p, steps, warmup, log)
+    res = time_forwards(p, steps, warmup, log, splits=splits)
     p.close()
     return p.w, res
 
@@ -611,7 +611,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fanout", choices=sorted(WORKLOADS))
-    ap.add_argument("--others", default="decode,prefill,mixed,join400,join8000,append",
+    ap.add_argument("--others", default="decode,decode_heuristic,prefill,mixed,join400,join8000,append",
                     help="comma list of secondary workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -690,6 +690,14 @@ def main():
     for name in [x for x in args.others.split(",") if x and x != args.workload]:
         if name == "append":
             others[name] = run_append(args.steps, 2, log)
+            continue
+        if name == "decode_heuristic":
+            # The 8k decode with every shard count left to the library (the
+            # workload as specified pins 32 shards).
+            wo, ro = run_workload(WORKLOADS["decode"], args.steps, 2, log, splits=None)
+            ro["roofline"] = roofline_of(wo, ro, None)
+            ro["note"] = "decode_8k with the library's own shard choice instead of the pinned 32"
+            others[name] = ro
             continue
         # Long workloads get fewer timed steps, so the default run stays short.
         long_wl = name in ("prefill", "mixed", "join8000")
