@@ -309,9 +309,7 @@ def cpu_baseline(name: str, budget_s: float, log):
     import torch
 
     import oracle
-    from workload import generate, get_workload
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import cpu_subset
+    from workload import cpu_subset, generate, get_workload
 
     w = get_workload(name)
     torch.set_num_threads(os.cpu_count() or 1)

@@ -22,6 +22,6 @@ parity-unpinned.
 
 from .fp64 import (  # noqa: F401
     kv_head_of, default_scale, lse_of, query_positions, key_visible, private_location, append_kv,
-    branch_context, attention, partial_state, merge_states, finalize,
+    branch_context, attention, sample_slots, heads_of_kv, partial_state, merge_states, finalize,
     EMPTY_LSE,
 )

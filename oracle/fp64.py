@@ -155,16 +155,34 @@ def _softmax_rows(z: torch.Tensor, v: torch.Tensor):
     return o, lse.squeeze(-1)
 
 
+def sample_slots(items: Sequence[int]) -> dict:
+    """Output slot of each requested token (or head) id: its place in the
+    list as the caller gave it (any order, any subset)."""
+    return {x: i for i, x in enumerate(items)}
+
+
+def heads_of_kv(kv: int, num_q_heads: int, num_kv_heads: int) -> List[int]:
+    """The query heads that read KV head kv, through kv_head_of."""
+    return [h for h in range(num_q_heads) if kv_head_of(h, num_q_heads, num_kv_heads) == kv]
+
+
 def attention(inp, num_kv_heads: int, page_size: int, causal: bool,
               softmax_scale: Optional[float] = None,
               tokens: Optional[Sequence[int]] = None,
-              heads: Optional[Sequence[int]] = None,
-              max_block: int = 1 << 22):
+              heads: Optional[Sequence[int]] = None):
     """O [n_tok, H_q, d] and LSE [n_tok, H_q] in float64.
 
-    ``tokens`` (global query-token indices) and ``heads`` restrict the
-    computation to a sample; the returned tensors then have shape
-    [len(tokens), len(heads), d] and [len(tokens), len(heads)].
+    ``tokens`` (global query-token indices, any order, any branches) and
+    ``heads`` restrict the computation to a sample; the returned tensors
+    then have shape [len(tokens), len(heads), d] and [len(tokens),
+    len(heads)], in the order given.
+
+    Every value comes from the same computation whether it is requested
+    alone or with all others: the unit of work is one query token against
+    one KV head, i.e. the scores of that token's query heads of the KV head
+    over the branch's whole context (one fixed-shape product with the KV
+    head's keys, then one with its values). A sample therefore returns
+    exactly the matching entries of the full call.
     """
     n_tok, H_q, d = inp.q.shape
     scale = default_scale(d) if softmax_scale is None else softmax_scale
@@ -173,32 +191,33 @@ def attention(inp, num_kv_heads: int, page_size: int, causal: bool,
     head_list = list(range(H_q)) if heads is None else list(heads)
     out_o = torch.zeros(len(tok_list), len(head_list), d, dtype=F64)
     out_l = torch.full((len(tok_list), len(head_list)), EMPTY_LSE, dtype=F64)
-    where = {t: i for i, t in enumerate(tok_list)}
+    row_of = sample_slots(tok_list)
+    col_of = sample_slots(head_list)
+    kv_list = sorted({kv_head_of(h, H_q, num_kv_heads) for h in head_list})
     for b in range(len(inp.branch_q_len)):
         T = inp.branch_q_len[b]
-        if T == 0:
-            continue
-        mine = [t for t in range(q_begin[b], q_begin[b] + T) if t in where]
+        mine = [t for t in range(q_begin[b], q_begin[b] + T) if t in row_of]
         if not mine:
             continue
         kb, vb = branch_context(inp, b, page_size)
         C = kb.shape[0]
         qpos_all = query_positions(C, T)
         kpos = torch.arange(C, dtype=torch.int64)
-        chunk = max(1, max_block // max(1, C))
-        for c0 in range(0, len(mine), chunk):
-            toks = mine[c0:c0 + chunk]
-            local = torch.tensor([t - q_begin[b] for t in toks], dtype=torch.int64)
-            qrows = inp.q[torch.tensor(toks, device=inp.q.device)].to("cpu", F64)   # [n, H_q, d]
-            vis = key_visible(kpos, qpos_all[local], causal)                       # [n, C]
-            for hi, h in enumerate(head_list):
-                kv = kv_head_of(h, H_q, num_kv_heads)
-                z = scale * (qrows[:, h, :] @ kb[:, kv, :].T)                     # [n, C]
+        for kv in kv_list:
+            k_kv = kb[:, kv, :].contiguous()             # [C, d]
+            v_kv = vb[:, kv, :].contiguous()
+            hs = heads_of_kv(kv, H_q, num_kv_heads)
+            wanted = [(i, h) for i, h in enumerate(hs) if h in col_of]
+            hsel = torch.tensor(hs, dtype=torch.int64, device=inp.q.device)
+            for t in mine:
+                q_blk = inp.q[t].index_select(0, hsel).to("cpu", F64).contiguous()   # [len(hs), d]
+                vis = key_visible(kpos, qpos_all[t - q_begin[b]].view(1), causal)  # [1, C]
+                z = scale * (q_blk @ k_kv.T)                                       # [len(hs), C]
                 z = z.masked_fill(~vis, float("-inf"))
-                o, lse = _softmax_rows(z, vb[:, kv, :])
-                rows = torch.tensor([where[t] for t in toks])
-                out_o[rows, hi] = o
-                out_l[rows, hi] = lse
+                o, lse = _softmax_rows(z, v_kv)
+                for i, h in wanted:
+                    out_o[row_of[t], col_of[h]] = o[i]
+                    out_l[row_of[t], col_of[h]] = lse[i]
     return out_o, out_l
 
 

@@ -463,13 +463,51 @@ def pin_invariant_append_then_attend():
     assert torch.equal(o2, o) and torch.equal(l2, lse)
 
 
+def pin_sampled_mode_equals_full_call():
+    """A sampled call -- any subset of query tokens across branches and
+    groups, any subset of query heads, in any order -- returns exactly the
+    matching entries of the full call, bit for bit. Batching and sampling
+    change only which rows are computed, never their value (ADR-0060 GQA
+    fused attention, Algorithm lineage: no new mathematics; AHBM Agentic
+    Runtime Architecture, §1.3: combined rows stay independent). Every
+    full-size GPU parity test relies on this mode."""
+    cases = [
+        custom("sample_fanout", H_q=8, H_kv=2, d=16, page_size=4, shared=(23,),
+               branches=((0, 5, 9), (0, 3, 14), (0, 6, 2)), seed=37),
+        # two groups (an empty one holding independent requests) and a
+        # zero-query branch between them
+        custom("sample_groups", H_q=6, H_kv=3, d=8, page_size=3, shared=(0, 19),
+               branches=((0, 1, 11), (0, 1, 4), (1, 0, 5), (1, 4, 7), (1, 2, 3)), seed=41),
+        get_workload("tiny_fp32_fanout"),
+    ]
+    for w in cases:
+        inp = generate(w, "cpu")
+        o, lse = run_oracle(w, inp)
+        n, H = o.shape[0], o.shape[1]
+        rng = random.Random(w.seed)
+        samples = [
+            (list(range(n))[::-1], None),                       # every token, reversed
+            (rng.sample(range(n), max(1, n // 2)), None),        # a shuffled subset across branches
+            (None, list(range(H))[::-1]),                       # every head, reversed
+            (rng.sample(range(n), max(1, n // 3)), rng.sample(range(H), max(1, H // 2))),
+            ([n - 1], [0]),                                     # one entry
+            ([0, n - 1], [H - 1, 0]),
+        ]
+        for toks, heads in samples:
+            o2, l2 = run_oracle(w, inp, tokens=toks, heads=heads)
+            ti = torch.tensor(list(range(n)) if toks is None else toks, dtype=torch.int64)
+            hi = torch.tensor(list(range(H)) if heads is None else heads, dtype=torch.int64)
+            assert torch.equal(o2, o[ti][:, hi]), (w.name, toks, heads)
+            assert torch.equal(l2, lse[ti][:, hi]), (w.name, toks, heads)
+
+
 ALL_PINS = [
     pin_golden_weights_123, pin_golden_paged_causal, pin_golden_merge,
     pin_brute_force_tiny, pin_library_sdpa, pin_closed_form_zero_q,
     pin_closed_form_prefill_row0, pin_closed_form_dominant_key,
     pin_invariant_batching, pin_invariant_split_merge, pin_invariant_causal,
     pin_invariant_gqa_map, pin_invariant_paging, pin_golden_append_placement,
-    pin_invariant_append_then_attend,
+    pin_invariant_append_then_attend, pin_sampled_mode_equals_full_call,
 ]
 
 

@@ -42,6 +42,16 @@ ORIGINAL_APPEND = OA.append_kv
 def _append_from_front(k_pages, v_pages, table, private_len, n_new, k_new, v_new, ps):
     return ORIGINAL_APPEND(k_pages, v_pages, table, [0] * len(n_new), n_new, k_new, v_new, ps)
 
+def _slots_in_sorted_order(items):
+    # right for a full call or an in-order sample, wrong for any other order
+    return {x: i for i, x in enumerate(sorted(items))}
+
+
+def _slots_first_only(items):
+    # every requested id after the first lands on the slot of the one before it
+    return {x: max(0, i - 1) for i, x in enumerate(items)}
+
+
 MUTATIONS = {
     "gqa_interleaved_heads": ("kv_head_of", lambda h, hq, hkv: h % hkv),
     "queries_at_first_positions": ("query_positions", lambda C, T: torch.arange(0, T)),
@@ -59,6 +69,8 @@ MUTATIONS = {
     "merge_drops_rescale": ("merge_states", _merge_drop_b_scale),
     "k_and_v_swapped": ("branch_context", _branch_context_swapped),
     "append_from_slot_zero": ("append_kv", _append_from_front),
+    "sample_slots_sorted": ("sample_slots", _slots_in_sorted_order),
+    "sample_slots_shifted": ("sample_slots", _slots_first_only),
 }
 
 

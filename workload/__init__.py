@@ -8,3 +8,4 @@ without sharing any code of the method.
 
 from .configs import Workload, WORKLOADS, get_workload, custom, Branch, Group  # noqa: F401
 from .generate import generate, Inputs  # noqa: F401
+from .subset import cpu_subset  # noqa: F401
