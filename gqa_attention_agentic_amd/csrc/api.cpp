@@ -1,19 +1,27 @@
 // C ABI of the shared-prefix GQA attention library (declared in gqa_attn.h).
 //
 // A forward call validates its arguments on the host, builds (or reuses) the
-// plan, copies it to the device through pinned staging with one async copy,
-// and launches up to three kernels: the MFMA-bound (wide) attention kernel,
-// the 32-row (narrow) attention kernel and the LSE merge, all ordered on the
-// caller's stream. When a forward has items of both attention kernels, the
-// narrow one runs on the handle's side stream, forked from and joined back
-// into the caller's stream with events, so that the two run side by side on
-// the compute units the plan gives each. It never synchronises the stream;
-// the only allocations happen when the plan or the partial workspace
-// outgrows what the handle already holds (and the side stream and its two
-// events, created at the first forward that needs them).
+// plan, makes sure its device buffers are large enough, copies the plan to
+// the device with one async copy when it changed, and launches up to three
+// kernels: the MFMA-bound (wide) attention kernel, the 32-row (narrow)
+// attention kernel and the LSE merge, all ordered on the caller's stream.
+// When a forward has items of both attention kernels, the narrow one runs on
+// the handle's side stream, forked from and joined back into the caller's
+// stream with events, so that the two run side by side on the compute units
+// the plan gives each. It never synchronises the stream. Everything that can
+// fail for a reason other than a launch (arguments, metadata, allocation) is
+// settled before the first launch.
+//
+// The handle's device buffers: the plan, the arrival counters of the
+// in-launch combination (zero between forwards: every forward leaves them
+// so), and the partial workspace. A buffer that a forward under HIP graph
+// capture referenced is never rewritten with other contents nor freed before
+// the handle is destroyed, so a captured graph stays valid after later
+// forwards with other metadata.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -48,6 +56,24 @@ struct TimerSlot {
   bool wide, narrow, merged, concurrent;
 };
 
+// A device buffer of the handle. `captured`: a forward made under HIP graph
+// capture references it, so it keeps its contents' meaning and its memory
+// until the handle is destroyed.
+struct DevBuf {
+  char* p = nullptr;
+  size_t cap = 0;
+  bool captured = false;
+};
+
+// Byte offsets of the serialised plan: wide items | narrow items | wide bins
+// | narrow bins | token records | combination records (each 256-B aligned).
+struct PlanLayout {
+  size_t wide = 0, narrow = 0, wide_bins = 0, narrow_bins = 0, tok_rec = 0, combs = 0, bytes = 0;
+};
+
+// Every plan a handle builds gets a process-unique id.
+std::atomic<uint64_t> g_next_plan_id{1};
+
 }  // namespace
 
 struct gqa_attn {
@@ -55,22 +81,22 @@ struct gqa_attn {
   int device = 0;
   int n_cu = 256;
   int wide_per_cu = 1, narrow_per_cu = 1;   // resident workgroups per CU of each attention kernel
-  // plan cache
+  // plan cache (host)
   std::vector<int32_t> key;
   gqa::Plan plan;
   bool have_plan = false;
-  // device plan buffer and its pinned staging
-  char* d_plan = nullptr;
-  size_t d_plan_cap = 0;
+  uint64_t plan_id = 0;
+  // device copy of plan `d_plan_id` and its pinned staging
+  DevBuf d_plan;
+  uint64_t d_plan_id = 0;
   char* h_staging = nullptr;
   size_t h_staging_cap = 0;
   hipEvent_t staging_free = nullptr;   // recorded after the last staging -> device copy
-  size_t off_wide = 0, off_narrow = 0, off_wide_bins = 0, off_narrow_bins = 0, off_tok_rec = 0, off_combs = 0;
-  // workspace: arrival counters (one per query token and KV head), then the
-  // partial (m, l) and O rows
-  char* d_work = nullptr;
-  bool counters_dirty = true;   // counters must be cleared before the next launch
-  size_t d_work_cap = 0;
+  // arrival counters (one per query token and KV head) and partial workspace
+  // ((m, l) rows, then O rows)
+  DevBuf d_counters;
+  DevBuf d_work;
+  std::vector<char*> retired;          // buffers a captured graph may still read
   // K/V append: per-row (branch, position) list on the device, and a ring
   // of pinned staging slots, each with the event after which it may be
   // rewritten (the host waits only for the upload of four calls back)
@@ -157,99 +183,72 @@ void fill_stats(const gqa::Plan& P, int64_t D, gqa_plan_stats* s) {
   s->narrow_cus = P.narrow_cus;
 }
 
-// Serialised plan: wide items | narrow items | wide bins | narrow bins |
-// token records | combination records.
-size_t plan_layout(gqa_attn* h) {
-  const gqa::Plan& P = h->plan;
+PlanLayout plan_layout(const gqa::Plan& P) {
+  PlanLayout L;
   size_t off = 0;
-  h->off_wide = off;
+  L.wide = off;
   off = align_up(off + P.wide.size() * sizeof(gqa::WorkItem), 256);
-  h->off_narrow = off;
+  L.narrow = off;
   off = align_up(off + P.narrow.size() * sizeof(gqa::WorkItem), 256);
-  h->off_wide_bins = off;
+  L.wide_bins = off;
   off = align_up(off + P.wide_bins.size() * sizeof(int32_t), 256);
-  h->off_narrow_bins = off;
+  L.narrow_bins = off;
   off = align_up(off + P.narrow_bins.size() * sizeof(int32_t), 256);
-  h->off_tok_rec = off;
+  L.tok_rec = off;
   off = align_up(off + P.tok_rec.size() * sizeof(gqa::TokRec), 256);
-  h->off_combs = off;
+  L.combs = off;
   off = align_up(off + P.combs.size() * sizeof(gqa::CombTok), 256);
-  return std::max<size_t>(off, 256);
+  L.bytes = std::max<size_t>(off, 256);
+  return L;
 }
 
-gqa_status upload_plan(gqa_attn* h, hipStream_t stream) {
-  const size_t bytes = plan_layout(h);
-  hipError_t e;
-  // The staging buffer may still feed the previous copy.
-  if (h->staging_free) {
-    e = hipEventSynchronize(h->staging_free);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-  }
-  if (bytes > h->h_staging_cap) {
-    if (h->h_staging) hipHostFree(h->h_staging);
-    h->h_staging = nullptr;
-    h->h_staging_cap = 0;
-    e = hipHostMalloc((void**)&h->h_staging, bytes, hipHostMallocDefault);
-    if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "pinned plan staging allocation failed");
-    h->h_staging_cap = bytes;
-  }
-  if (bytes > h->d_plan_cap) {
-    if (h->d_plan) {
-      e = hipFree(h->d_plan);   // synchronises the device: no kernel still reads it
-      if (e != hipSuccess) return hip_fail(e, "hipFree(plan)");
-    }
-    h->d_plan = nullptr;
-    h->d_plan_cap = 0;
-    e = hipMalloc((void**)&h->d_plan, bytes);
-    if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "device plan allocation failed");
-    h->d_plan_cap = bytes;
-  }
-  const gqa::Plan& P = h->plan;
+void serialise_plan(const gqa::Plan& P, const PlanLayout& L, char* dst) {
   auto put = [&](size_t off, const void* src, size_t n) {
-    if (n) std::memcpy(h->h_staging + off, src, n);
+    if (n) std::memcpy(dst + off, src, n);
   };
-  put(h->off_wide, P.wide.data(), P.wide.size() * sizeof(gqa::WorkItem));
-  put(h->off_narrow, P.narrow.data(), P.narrow.size() * sizeof(gqa::WorkItem));
-  put(h->off_wide_bins, P.wide_bins.data(), P.wide_bins.size() * sizeof(int32_t));
-  put(h->off_narrow_bins, P.narrow_bins.data(), P.narrow_bins.size() * sizeof(int32_t));
-  put(h->off_tok_rec, P.tok_rec.data(), P.tok_rec.size() * sizeof(gqa::TokRec));
-  put(h->off_combs, P.combs.data(), P.combs.size() * sizeof(gqa::CombTok));
-  e = hipMemcpyAsync(h->d_plan, h->h_staging, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
-  if (!h->staging_free) {
-    e = hipEventCreateWithFlags(&h->staging_free, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  }
-  e = hipEventRecord(h->staging_free, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  return GQA_OK;
+  put(L.wide, P.wide.data(), P.wide.size() * sizeof(gqa::WorkItem));
+  put(L.narrow, P.narrow.data(), P.narrow.size() * sizeof(gqa::WorkItem));
+  put(L.wide_bins, P.wide_bins.data(), P.wide_bins.size() * sizeof(int32_t));
+  put(L.narrow_bins, P.narrow_bins.data(), P.narrow_bins.size() * sizeof(int32_t));
+  put(L.tok_rec, P.tok_rec.data(), P.tok_rec.size() * sizeof(gqa::TokRec));
+  put(L.combs, P.combs.data(), P.combs.size() * sizeof(gqa::CombTok));
 }
 
-// Bytes of the arrival counters at the start of the workspace.
-size_t counter_bytes(const gqa_attn* h) {
-  return h->plan.part_rows ? align_up((size_t)h->plan.n_q_tokens * h->p.num_kv_heads * sizeof(int32_t), 256) : 0;
+// Bytes of the arrival counters (one per query token and KV head) and of the
+// partial workspace ((m, l) rows, then O rows) that a plan needs.
+size_t counter_bytes(const gqa::Plan& P, int H_kv) {
+  return P.part_rows ? align_up((size_t)P.n_q_tokens * H_kv * sizeof(int32_t), 256) : 0;
+}
+size_t ml_bytes(const gqa::Plan& P) { return align_up((size_t)P.part_rows * sizeof(float2), 256); }
+size_t work_bytes(const gqa::Plan& P, int D) {
+  return P.part_rows ? ml_bytes(P) + (size_t)P.part_rows * D * sizeof(float) : 0;
 }
 
-gqa_status ensure_workspace(gqa_attn* h) {
-  const size_t rows = (size_t)h->plan.part_rows;
-  const size_t need = rows ? counter_bytes(h) + align_up(rows * sizeof(float2), 256) +
-                                 rows * (size_t)h->p.head_dim * sizeof(float)
-                           : 0;
-  if (h->p.workspace_bytes_cap > 0 && need > (size_t)h->p.workspace_bytes_cap)
-    return fail(GQA_ERR_NO_MEMORY, "partial workspace of " + std::to_string(need) +
-                                       " bytes exceeds workspace_bytes_cap");
-  if (need <= h->d_work_cap) return GQA_OK;
-  hipError_t e;
-  if (h->d_work) {
-    e = hipFree(h->d_work);
-    if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+// Makes `b` hold at least `need` bytes; a buffer that must keep its
+// contents' meaning (captured, or `replace` for a plan that differs) is
+// retired rather than reused or freed. *fresh tells whether a new buffer
+// was allocated.
+gqa_status ensure_buf(gqa_attn* h, DevBuf& b, size_t need, bool replace, const char* what, bool* fresh) {
+  if (fresh) *fresh = false;
+  if (need == 0) return GQA_OK;
+  if (need <= b.cap && !(replace && b.captured)) return GQA_OK;
+  if (b.p) {
+    if (b.captured) {
+      h->retired.push_back(b.p);
+    } else {
+      hipError_t e = hipFree(b.p);   // synchronises the device: no kernel still reads it
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
   }
-  h->d_work = nullptr;
-  h->d_work_cap = 0;
-  e = hipMalloc((void**)&h->d_work, need);
-  if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "workspace allocation of " + std::to_string(need) + " bytes failed");
-  h->d_work_cap = need;
-  h->counters_dirty = true;
+  b = DevBuf();
+  const size_t cap = std::max(need, (size_t)256);
+  hipError_t e = hipMalloc((void**)&b.p, cap);
+  if (e != hipSuccess) {
+    b.p = nullptr;
+    return fail(GQA_ERR_NO_MEMORY, std::string(what) + " allocation of " + std::to_string(cap) + " bytes failed");
+  }
+  b.cap = cap;
+  if (fresh) *fresh = true;
   return GQA_OK;
 }
 
@@ -265,6 +264,245 @@ TimerSlot* next_timer(gqa_attn* h) {
     h->timers.push_back(t);
   }
   return &h->timers[h->timers_used++];
+}
+
+struct ForwardArgs {
+  const void *q, *k_shared, *v_shared;
+  int32_t n_shared_tokens;
+  const void *k_pages, *v_pages;
+  const int32_t* page_table;
+  int32_t max_pages_per_branch;
+  int32_t n_groups;
+  const int32_t *group_shared_start, *group_shared_len;
+  int32_t n_branches;
+  const int32_t *branch_group, *branch_q_len, *branch_private_len, *splits_override;
+  int32_t causal;
+  void* o;
+  float* lse;
+  void* stream;
+};
+
+// Where a forward's plan, counters and partials live on the device.
+struct DevRegions {
+  const char* plan;
+  int32_t* counters;
+  char* work;
+};
+
+// The kernel launches of one forward (the plan is on the device already).
+gqa_status launch_forward(gqa_attn* h, const ForwardArgs& f, const gqa::Plan& Q, const PlanLayout& L,
+                          const DevRegions& R, hipStream_t st, TimerSlot* tm, bool use_side) {
+  gqa::AttnArgs a{};
+  a.q = f.q;
+  a.k_shared = f.k_shared;
+  a.v_shared = f.v_shared;
+  a.k_pages = f.k_pages;
+  a.v_pages = f.v_pages;
+  a.page_table = f.page_table;
+  a.tok_rec = (const gqa::TokRec*)(R.plan + L.tok_rec);
+  a.combs = (const gqa::CombTok*)(R.plan + L.combs);
+  a.counters = R.counters;
+  a.part_ml = (float2*)R.work;
+  a.part_o = (float*)(R.work + ml_bytes(Q));
+  a.o = f.o;
+  a.lse = f.lse;
+  a.max_pages = f.max_pages_per_branch;
+  a.H_q = h->p.num_q_heads;
+  a.H_kv = h->p.num_kv_heads;
+  a.G = a.H_q / a.H_kv;
+  a.n_shared = f.n_shared_tokens;
+  a.page_size = h->p.page_size;
+  a.page_shift = -1;
+  for (int sft = 0; sft < 13; ++sft)
+    if ((1 << sft) == h->p.page_size) a.page_shift = sft;
+  a.causal = f.causal;
+  a.n_q_tokens = Q.n_q_tokens;
+  a.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
+
+  auto ev = [&](int k) -> hipEvent_t { return tm ? tm->ev[k] : nullptr; };
+  if (tm) {
+    tm->wide = !Q.wide.empty();
+    tm->narrow = !Q.narrow.empty();
+    tm->merged = Q.merge_launch;
+    tm->concurrent = Q.concurrent && use_side;
+  }
+  hipError_t e;
+  const bool side_by_side = Q.concurrent && use_side;
+  if (side_by_side) {
+    // Narrow kernel on the side stream, after everything already queued on
+    // the caller's stream (plan upload, counter clear); the caller's stream
+    // waits for it before the merge. Both streams have the default priority.
+    e = hipEventRecord(h->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "fork to the side stream");
+    a.items = (const gqa::WorkItem*)(R.plan + L.narrow);
+    a.bins = (const int32_t*)(R.plan + L.narrow_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, h->side,
+                              ev(2), ev(3));
+    if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
+    e = hipEventRecord(h->join, h->side);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(join)");
+    a.items = (const gqa::WorkItem*)(R.plan + L.wide);
+    a.bins = (const int32_t*)(R.plan + L.wide_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
+                              ev(1));
+    // The caller's stream waits for the narrow kernel even when the wide
+    // launch failed, so that no later work on it overlaps a kernel still
+    // writing the outputs.
+    const hipError_t ej = hipStreamWaitEvent(st, h->join, 0);
+    if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
+    if (ej != hipSuccess) return hip_fail(ej, "join from the side stream");
+  } else if (!Q.wide.empty()) {
+    a.items = (const gqa::WorkItem*)(R.plan + L.wide);
+    a.bins = (const int32_t*)(R.plan + L.wide_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
+                              ev(1));
+    if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
+  }
+  if (!side_by_side && !Q.narrow.empty()) {
+    a.items = (const gqa::WorkItem*)(R.plan + L.narrow);
+    a.bins = (const int32_t*)(R.plan + L.narrow_bins);
+    e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, st, ev(2),
+                              ev(3));
+    if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
+  }
+  if (Q.merge_launch) {
+    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, Q.max_row_parts, st, ev(4), ev(5));
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return GQA_OK;
+}
+
+gqa_status forward_impl(gqa_attn* h, const ForwardArgs& f) {
+  if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  gqa::PlanInput in;
+  gqa_status s = make_input(&h->p, f.n_groups, f.group_shared_start, f.group_shared_len, f.n_branches,
+                            f.branch_group, f.branch_q_len, f.branch_private_len, f.splits_override, f.causal,
+                            h->n_cu, h->wide_per_cu, h->narrow_per_cu, &in);
+  if (s != GQA_OK) return s;
+
+  // Plan cache key: every input of the planner.
+  std::vector<int32_t> key;
+  key.reserve(8 + 2 * f.n_groups + 4 * f.n_branches);
+  key.push_back(f.n_groups);
+  key.push_back(f.n_branches);
+  key.push_back(f.causal);
+  key.push_back(f.splits_override ? 1 : 0);
+  key.insert(key.end(), in.g_start.begin(), in.g_start.end());
+  key.insert(key.end(), in.g_len.begin(), in.g_len.end());
+  key.insert(key.end(), in.b_group.begin(), in.b_group.end());
+  key.insert(key.end(), in.b_qlen.begin(), in.b_qlen.end());
+  key.insert(key.end(), in.b_priv.begin(), in.b_priv.end());
+  key.insert(key.end(), in.splits_override.begin(), in.splits_override.end());
+  const bool same = h->have_plan && key == h->key;
+  gqa::Plan fresh;
+  const gqa::Plan& P = same ? h->plan : fresh;
+  if (!same) {
+    std::string err = gqa::build_plan(in, &fresh);
+    if (!err.empty()) return fail(GQA_ERR_INVALID_ARG, err);
+  }
+
+  // Pointer checks against the (new) plan's extents.
+  const bool any_q = P.n_q_tokens > 0;
+  bool any_priv = false;
+  for (int32_t b = 0; b < f.n_branches; ++b) any_priv |= in.b_priv[b] > 0;
+  if (any_q && (!f.q || !f.o || !f.lse)) return fail(GQA_ERR_INVALID_ARG, "q, o and lse must be non-NULL");
+  if (P.n_shared_tokens > 0 && (!f.k_shared || !f.v_shared))
+    return fail(GQA_ERR_INVALID_ARG, "k_shared and v_shared must be non-NULL");
+  if (f.n_shared_tokens < P.n_shared_tokens)
+    return fail(GQA_ERR_INVALID_ARG, "a group's shared range ends past n_shared_tokens");
+  if (any_priv && (!f.k_pages || !f.v_pages || !f.page_table))
+    return fail(GQA_ERR_INVALID_ARG, "k_pages, v_pages and page_table must be non-NULL");
+  if (any_priv && f.max_pages_per_branch < P.max_branch_pages)
+    return fail(GQA_ERR_INVALID_ARG, "max_pages_per_branch is smaller than a branch's page count");
+  const void* ptrs[] = {f.q, f.k_shared, f.v_shared, f.k_pages, f.v_pages, f.o};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(GQA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if ((f.page_table && (reinterpret_cast<uintptr_t>(f.page_table) & 3u)) ||
+      (f.lse && (reinterpret_cast<uintptr_t>(f.lse) & 3u)))
+    return fail(GQA_ERR_INVALID_ARG, "page_table and lse must be 4-byte aligned");
+  if (!any_q) return GQA_OK;
+
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  hipStream_t st = (hipStream_t)f.stream;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(st, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  const bool capturing = cs != hipStreamCaptureStatusNone;
+
+  const PlanLayout L = plan_layout(P);
+  const int H_kv = h->p.num_kv_heads, D = h->p.head_dim;
+  const size_t cnt_need = counter_bytes(P, H_kv), work_need = work_bytes(P, D);
+  const char* under_capture =
+      "under HIP graph capture a forward must reuse the plan and buffers of an earlier forward with the "
+      "same metadata: make one outside capture first";
+  if (h->p.workspace_bytes_cap > 0 && cnt_need + work_need > (size_t)h->p.workspace_bytes_cap)
+    return fail(GQA_ERR_NO_MEMORY, "partial workspace of " + std::to_string(cnt_need + work_need) +
+                                       " bytes exceeds workspace_bytes_cap");
+  if (capturing && (!same || h->d_plan_id != h->plan_id || cnt_need > h->d_counters.cap ||
+                    work_need > h->d_work.cap || (P.concurrent && !h->side)))
+    return fail(GQA_ERR_INVALID_ARG, under_capture);
+
+  // The host plan is committed; from here on a failure leaves it cached
+  // (it is valid) and the device copy marked stale.
+  if (!same) {
+    h->plan = std::move(fresh);
+    h->key = std::move(key);
+    h->have_plan = true;
+    h->plan_id = g_next_plan_id.fetch_add(1);
+  }
+  const gqa::Plan& Q = h->plan;
+  const bool upload = h->d_plan_id != h->plan_id;
+
+  DevRegions R{};
+  bool clear_counters = false;
+  // Every allocation before the first launch.
+  s = ensure_buf(h, h->d_counters, cnt_need, false, "counter", &clear_counters);
+  if (s == GQA_OK) s = ensure_buf(h, h->d_work, work_need, false, "workspace", nullptr);
+  if (s == GQA_OK && upload) s = ensure_buf(h, h->d_plan, L.bytes, true, "device plan", nullptr);
+  if (s != GQA_OK) return s;
+  if (upload) {
+    if (h->staging_free) {   // the staging buffer may still feed the previous copy
+      e = hipEventSynchronize(h->staging_free);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    } else {
+      e = hipEventCreateWithFlags(&h->staging_free, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    if (L.bytes > h->h_staging_cap) {
+      if (h->h_staging) hipHostFree(h->h_staging);
+      h->h_staging = nullptr;
+      h->h_staging_cap = 0;
+      e = hipHostMalloc((void**)&h->h_staging, L.bytes, hipHostMallocDefault);
+      if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "pinned plan staging allocation failed");
+      h->h_staging_cap = L.bytes;
+    }
+  }
+  if (Q.concurrent && !h->side) {
+    e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "side stream creation");
+  }
+  // Launches.
+  if (clear_counters) {
+    e = gqa::launch_zero_i32((int32_t*)h->d_counters.p, (int64_t)(h->d_counters.cap / sizeof(int32_t)), st);
+    if (e != hipSuccess) return hip_fail(e, "counter clear");
+  }
+  if (upload) {
+    serialise_plan(Q, L, h->h_staging);
+    e = hipMemcpyAsync(h->d_plan.p, h->h_staging, L.bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipEventRecord(h->staging_free, st);
+    if (e != hipSuccess) return hip_fail(e, "plan upload");
+    h->d_plan_id = h->plan_id;
+  }
+  if (capturing) h->d_plan.captured = h->d_counters.captured = h->d_work.captured = true;
+  R.plan = h->d_plan.p;
+  R.counters = (int32_t*)h->d_counters.p;
+  R.work = h->d_work.p;
+  TimerSlot* tm = (h->timing && !capturing) ? next_timer(h) : nullptr;
+  return launch_forward(h, f, Q, L, R, st, tm, h->side != nullptr);
 }
 
 }  // namespace
@@ -303,8 +541,9 @@ gqa_status gqa_attn_destroy(gqa_attn* h) {
   if (!h) return GQA_OK;
   hipSetDevice(h->device);
   hipDeviceSynchronize();
-  if (h->d_plan) hipFree(h->d_plan);
-  if (h->d_work) hipFree(h->d_work);
+  for (DevBuf* b : {&h->d_plan, &h->d_counters, &h->d_work})
+    if (b->p) hipFree(b->p);
+  for (char* p : h->retired) hipFree(p);
   if (h->h_staging) hipHostFree(h->h_staging);
   if (h->staging_free) hipEventDestroy(h->staging_free);
   if (h->side) hipStreamDestroy(h->side);
@@ -332,166 +571,12 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
                             int32_t n_branches, const int32_t* branch_group, const int32_t* branch_q_len,
                             const int32_t* branch_private_len, const int32_t* splits_override,
                             int32_t causal, void* o, float* lse, void* stream) {
-  if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
-  gqa::PlanInput in;
-  gqa_status s = make_input(&h->p, n_groups, group_shared_start, group_shared_len, n_branches,
-                            branch_group, branch_q_len, branch_private_len, splits_override, causal,
-                            h->n_cu, h->wide_per_cu, h->narrow_per_cu, &in);
-  if (s != GQA_OK) return s;
-
-  // Plan cache key: every input of the planner.
-  std::vector<int32_t> key;
-  key.reserve(8 + 2 * n_groups + 4 * n_branches);
-  key.push_back(n_groups);
-  key.push_back(n_branches);
-  key.push_back(causal);
-  key.push_back(splits_override ? 1 : 0);
-  key.insert(key.end(), in.g_start.begin(), in.g_start.end());
-  key.insert(key.end(), in.g_len.begin(), in.g_len.end());
-  key.insert(key.end(), in.b_group.begin(), in.b_group.end());
-  key.insert(key.end(), in.b_qlen.begin(), in.b_qlen.end());
-  key.insert(key.end(), in.b_priv.begin(), in.b_priv.end());
-  key.insert(key.end(), in.splits_override.begin(), in.splits_override.end());
-  const bool same = h->have_plan && key == h->key;
-  gqa::Plan fresh;
-  const gqa::Plan& P = same ? h->plan : fresh;
-  if (!same) {
-    std::string err = gqa::build_plan(in, &fresh);
-    if (!err.empty()) return fail(GQA_ERR_INVALID_ARG, err);
-  }
-
-  // Pointer checks against the (new) plan's extents.
-  const bool any_q = P.n_q_tokens > 0;
-  bool any_priv = false;
-  for (int32_t b = 0; b < n_branches; ++b) any_priv |= in.b_priv[b] > 0;
-  if (any_q && (!q || !o || !lse)) return fail(GQA_ERR_INVALID_ARG, "q, o and lse must be non-NULL");
-  if (P.n_shared_tokens > 0 && (!k_shared || !v_shared))
-    return fail(GQA_ERR_INVALID_ARG, "k_shared and v_shared must be non-NULL");
-  if (n_shared_tokens < P.n_shared_tokens)
-    return fail(GQA_ERR_INVALID_ARG, "a group's shared range ends past n_shared_tokens");
-  if (any_priv && (!k_pages || !v_pages || !page_table))
-    return fail(GQA_ERR_INVALID_ARG, "k_pages, v_pages and page_table must be non-NULL");
-  if (any_priv && max_pages_per_branch < P.max_branch_pages)
-    return fail(GQA_ERR_INVALID_ARG, "max_pages_per_branch is smaller than a branch's page count");
-  const void* ptrs[] = {q, k_shared, v_shared, k_pages, v_pages, o};
-  for (const void* ptr : ptrs)
-    if (ptr && !aligned16(ptr)) return fail(GQA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-  if ((page_table && (reinterpret_cast<uintptr_t>(page_table) & 3u)) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-    return fail(GQA_ERR_INVALID_ARG, "page_table and lse must be 4-byte aligned");
-  if (!any_q) return GQA_OK;
-
-  hipError_t e = hipSetDevice(h->device);
-  if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
-  hipStream_t st = (hipStream_t)stream;
-  if (!same) {
-    h->plan = std::move(fresh);
-    h->key = std::move(key);
-    h->have_plan = true;
-    h->counters_dirty = true;   // the counter layout follows the plan
-    s = upload_plan(h, st);
-    if (s != GQA_OK) {
-      h->have_plan = false;
-      return s;
-    }
-  }
-  s = ensure_workspace(h);
-  if (s != GQA_OK) return s;
-  // Every forward leaves the counters at zero (the item that completes a
-  // token resets its counter); they are cleared here only after the plan or
-  // the workspace changed.
-  if (h->counters_dirty && counter_bytes(h) > 0) {
-    e = gqa::launch_zero_i32((int32_t*)h->d_work, (int64_t)(counter_bytes(h) / sizeof(int32_t)), st);
-    if (e != hipSuccess) return hip_fail(e, "counter clear");
-    h->counters_dirty = false;
-  }
-
-  const gqa::Plan& Q = h->plan;
-  gqa::AttnArgs a{};
-  a.q = q;
-  a.k_shared = k_shared;
-  a.v_shared = v_shared;
-  a.k_pages = k_pages;
-  a.v_pages = v_pages;
-  a.page_table = page_table;
-  a.tok_rec = (const gqa::TokRec*)(h->d_plan + h->off_tok_rec);
-  a.combs = (const gqa::CombTok*)(h->d_plan + h->off_combs);
-  a.counters = (int32_t*)h->d_work;
-  a.part_ml = (float2*)(h->d_work + counter_bytes(h));
-  a.part_o = (float*)(h->d_work + counter_bytes(h) + align_up((size_t)Q.part_rows * sizeof(float2), 256));
-  a.o = o;
-  a.lse = lse;
-  a.max_pages = max_pages_per_branch;
-  a.H_q = h->p.num_q_heads;
-  a.H_kv = h->p.num_kv_heads;
-  a.G = a.H_q / a.H_kv;
-  a.n_shared = n_shared_tokens;
-  a.page_size = h->p.page_size;
-  a.page_shift = -1;
-  for (int sft = 0; sft < 13; ++sft)
-    if ((1 << sft) == h->p.page_size) a.page_shift = sft;
-  a.causal = causal;
-  a.n_q_tokens = Q.n_q_tokens;
-  a.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
-
-  TimerSlot* tm = h->timing ? next_timer(h) : nullptr;
-  auto ev = [&](int k) -> hipEvent_t { return tm ? tm->ev[k] : nullptr; };
-  if (tm) {
-    tm->wide = !Q.wide.empty();
-    tm->narrow = !Q.narrow.empty();
-    tm->merged = Q.merge_launch;
-    tm->concurrent = Q.concurrent;
-  }
-  if (Q.concurrent) {
-    // Narrow kernel on the side stream, after everything already queued on
-    // the caller's stream (plan upload, counter clear); the caller's stream
-    // waits for it before the merge. Both streams have the default priority.
-    if (!h->side) {
-      e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
-      if (e != hipSuccess) return hip_fail(e, "side stream creation");
-    }
-    e = hipEventRecord(h->fork, st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
-    if (e != hipSuccess) return hip_fail(e, "fork to the side stream");
-    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
-    a.bins = (const int32_t*)(h->d_plan + h->off_narrow_bins);
-    e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, h->side,
-                              ev(2), ev(3));
-    if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
-    e = hipEventRecord(h->join, h->side);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(join)");
-    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
-    a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);
-    e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
-                              ev(1));
-    // The caller's stream waits for the narrow kernel even when the wide
-    // launch failed, so that no later work on it overlaps a kernel still
-    // writing the outputs.
-    const hipError_t ej = hipStreamWaitEvent(st, h->join, 0);
-    if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
-    if (ej != hipSuccess) return hip_fail(ej, "join from the side stream");
-  } else if (!Q.wide.empty()) {
-    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_wide);
-    a.bins = (const int32_t*)(h->d_plan + h->off_wide_bins);
-    e = gqa::launch_attention(a, (int32_t)Q.wide_bins.size() - 1, false, h->p.dtype, h->p.head_dim, st, ev(0),
-                              ev(1));
-    if (e != hipSuccess) return hip_fail(e, "attention (wide) launch");
-  }
-  if (!Q.concurrent && !Q.narrow.empty()) {
-    a.items = (const gqa::WorkItem*)(h->d_plan + h->off_narrow);
-    a.bins = (const int32_t*)(h->d_plan + h->off_narrow_bins);
-    e = gqa::launch_attention(a, (int32_t)Q.narrow_bins.size() - 1, true, h->p.dtype, h->p.head_dim, st, ev(2),
-                              ev(3));
-    if (e != hipSuccess) return hip_fail(e, "attention (narrow) launch");
-  }
-  if (Q.merge_launch) {
-    e = gqa::launch_merge(a, h->p.dtype, h->p.head_dim, Q.max_row_parts, st, ev(4), ev(5));
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
-  }
-  return GQA_OK;
+  const ForwardArgs f{q, k_shared, v_shared, n_shared_tokens, k_pages, v_pages, page_table, max_pages_per_branch,
+                      n_groups, group_shared_start, group_shared_len, n_branches, branch_group, branch_q_len,
+                      branch_private_len, splits_override, causal, o, lse, stream};
+  return forward_impl(h, f);
 }
+
 
 namespace {
 

@@ -427,27 +427,60 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   for (int32_t ui = 0; ui < nu; ++ui)
     if (override_of(ui) > 0) S[ui] = override_of(ui);
 
-  // Shard boundaries, live counts, workspace offsets, items.
+  // Shard boundaries and live shard counts per M-tile.
   P->api_splits.assign(ng + nb, 0);
   P->unit_slot = api_slot;
-  int64_t part = 0;
+  std::vector<std::vector<int32_t>> bounds(nu);
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
     const int32_t tile_keys = (u.bm != kNarrowRows) ? kWideKeys : kNarrowKeys;
-    std::vector<int32_t> bnd = shard_bounds(u.key_len, S[ui], tile_keys);
-    u.n_splits = (int32_t)bnd.size() - 1;
+    bounds[ui] = shard_bounds(u.key_len, S[ui], tile_keys);
+    u.n_splits = (int32_t)bounds[ui].size() - 1;
     P->api_splits[api_slot[ui]] = u.n_splits;
     P->max_splits = std::max(P->max_splits, u.n_splits);
     u.tile_off = (int32_t)P->tiles.size();
     for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
-      const int32_t kend = uw[ui].tile_key_end[t];
-      int32_t live = 0;
-      while (live < u.n_splits && bnd[live] < kend) ++live;
       TileInfo ti{};
-      ti.live = live;
-      ti.part_off = part;
-      part += (int64_t)in.H_kv * live * u.bm;
+      while (ti.live < u.n_splits && bounds[ui][ti.live] < uw[ui].tile_key_end[t]) ++ti.live;
+      ti.part_off = -1;
       P->tiles.push_back(ti);
+    }
+  }
+  // A tile's rows need workspace rows only if some token of the tile has two
+  // or more live partials over its prefix and suffix units; otherwise every
+  // row of the tile writes O / l directly.
+  std::vector<char> tile_needs(P->tiles.size(), 0);
+  for (int32_t b = 0; b < nb; ++b) {
+    const BranchDesc& br = P->branches[b];
+    const int32_t us[2] = {br.unit_sh, br.unit_pr};
+    for (int32_t t = 0; t < br.q_len; ++t) {
+      const int32_t tok = br.q_begin + t;
+      int32_t n = 0, tix[2] = {-1, -1};
+      for (int x = 0; x < 2; ++x) {
+        if (us[x] < 0) continue;
+        const UnitDesc& u = P->units[us[x]];
+        tix[x] = u.tile_off + (tok - u.tok_begin) / u.tpt;
+        n += P->tiles[tix[x]].live;
+      }
+      if (n >= 2)
+        for (int x = 0; x < 2; ++x)
+          if (tix[x] >= 0) tile_needs[tix[x]] = 1;
+    }
+  }
+  // Workspace offsets and items.
+  int64_t part = 0;
+  for (int32_t ui = 0; ui < nu; ++ui) {
+    UnitDesc& u = P->units[ui];
+    const int32_t tile_keys = (u.bm != kNarrowRows) ? kWideKeys : kNarrowKeys;
+    const std::vector<int32_t>& bnd = bounds[ui];
+    for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
+      const int32_t kend = uw[ui].tile_key_end[t];
+      TileInfo& ti = P->tiles[u.tile_off + t];
+      const int32_t live = ti.live;
+      if (tile_needs[u.tile_off + t]) {
+        ti.part_off = part;
+        part += (int64_t)in.H_kv * live * u.bm;
+      }
       const int32_t row_begin = (int32_t)(t * u.tpt * G);
       const int32_t n_rows = (int32_t)std::min<int64_t>(u.tpt, u.n_tok - (int64_t)t * u.tpt) * G;
       for (int32_t s = 0; s < live; ++s) {
@@ -465,7 +498,9 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           w.src = u.src;
           w.tok_begin = u.tok_begin;
           w.key_pos0 = u.key_pos0;
-          w.part_row = ti.part_off + ((int64_t)kv * live + s) * u.bm;
+          // Rows of a tile without workspace rows all write directly; the
+          // kernel never uses part_row for them.
+          w.part_row = ti.part_off >= 0 ? ti.part_off + ((int64_t)kv * live + s) * u.bm : 0;
           w.pad0 = w.pad1 = 0;
           P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
           (u.bm != kNarrowRows ? P->wide : P->narrow).push_back(w);

@@ -115,14 +115,26 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out);
  * uses must be a page of the pool); they are not checked on the device.
  * q, k/v and o must be 16-byte aligned, page_table and lse 4-byte aligned;
  * a pointer whose extent is zero may be NULL. Errors: GQA_ERR_INVALID_ARG, GQA_ERR_NO_MEMORY (workspace growth),
- * GQA_ERR_HIP (launch failure). The plan is rebuilt only when the metadata
- * differs from the previous call on this handle. A call whose plan is cached
- * (same metadata as the previous call, workspace already large enough)
- * issues only kernel launches and, when its two attention kernels run side
- * by side, the event fork / join of the handle's side stream: it allocates
- * nothing, uploads nothing and may be captured into a HIP graph. Replays of
- * such a graph share the handle's workspace with its other calls, so they
- * must be ordered with them on the device. */
+ * GQA_ERR_HIP (launch failure). On GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED
+ * and GQA_ERR_NO_MEMORY nothing was launched: arguments, metadata and every
+ * allocation are settled before the first launch.
+ *
+ * Plan and buffers: the plan is rebuilt only when the metadata differs from
+ * the previous call on this handle. The handle grows its device buffers (the
+ * plan, the arrival counters, the partial workspace) when a plan needs more
+ * than they hold. A call whose plan is cached (same metadata as the previous
+ * call, buffers already large enough) issues only kernel launches and, when
+ * its two attention kernels run side by side, the event fork / join of the
+ * handle's side stream: it allocates nothing and uploads nothing.
+ *
+ * HIP graph capture: a forward made while `stream` is capturing must be such
+ * a cached call; any other returns GQA_ERR_INVALID_ARG (make the same call
+ * once outside capture first). Buffers that a captured forward references
+ * are kept, unchanged in meaning, until the handle is destroyed: later
+ * forwards with other metadata get new buffers, so the graph stays valid.
+ * Its replays share the partial workspace and counters with the handle's
+ * other calls, so they must be ordered with them on the device. Timing
+ * events are not recorded under capture. */
 gqa_status gqa_attn_forward(gqa_attn* h,
                             const void* q,
                             const void* k_shared, const void* v_shared,

@@ -109,27 +109,29 @@ def append_kv(k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Te
 def branch_context(inp, b: int, page_size: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """K_b, V_b as float64 [C_b, H_kv, d]: the group's shared prefix followed
     by the branch's private suffix read through its page table
-    (AHBM Agentic Runtime Architecture, §3.1 branch page table)."""
+    (AHBM Agentic Runtime Architecture, §3.1 branch page table). The values
+    are stored KV-head-major, so that ``K_b[:, kv]`` is contiguous."""
     g = inp.branch_group[b]
     s0, sl = inp.group_shared_start[g], inp.group_shared_len[g]
-    ks = inp.k_shared[:, s0:s0 + sl, :].to("cpu", F64).permute(1, 0, 2)
-    vs = inp.v_shared[:, s0:s0 + sl, :].to("cpu", F64).permute(1, 0, 2)
     n_priv = inp.branch_private_len[b]
-    if n_priv == 0:
-        return ks.contiguous(), vs.contiguous()
-    table = inp.page_table[b].to("cpu").tolist()
-    pages, slots = [], []
-    for i in range(n_priv):
-        lp, slot = private_location(i, page_size)
-        pages.append(table[lp])
-        slots.append(slot)
-    pages_t = torch.tensor(pages, dtype=torch.int64)
-    slots_t = torch.tensor(slots, dtype=torch.int64)
-    kp = inp.k_pages[pages_t.to(inp.k_pages.device), :, slots_t.to(inp.k_pages.device), :]
-    vp = inp.v_pages[pages_t.to(inp.v_pages.device), :, slots_t.to(inp.v_pages.device), :]
-    kp = kp.to("cpu", F64)   # [n_priv, H_kv, d]
-    vp = vp.to("cpu", F64)
-    return torch.cat([ks, kp], 0), torch.cat([vs, vp], 0)
+    H_kv, d = inp.k_shared.shape[0], inp.k_shared.shape[2]
+    out = []
+    for src_shared, src_pages in ((inp.k_shared, inp.k_pages), (inp.v_shared, inp.v_pages)):
+        ctx = torch.empty(H_kv, sl + n_priv, d, dtype=F64)
+        ctx[:, :sl].copy_(src_shared[:, s0:s0 + sl, :])
+        if n_priv > 0:
+            table = inp.page_table[b].to("cpu").tolist()
+            pages, slots = [], []
+            for i in range(n_priv):
+                lp, slot = private_location(i, page_size)
+                pages.append(table[lp])
+                slots.append(slot)
+            pages_t = torch.tensor(pages, dtype=torch.int64, device=src_pages.device)
+            slots_t = torch.tensor(slots, dtype=torch.int64, device=src_pages.device)
+            priv = src_pages[pages_t, :, slots_t, :]              # [n_priv, H_kv, d]
+            ctx[:, sl:].copy_(priv.permute(1, 0, 2))
+        out.append(ctx.permute(1, 0, 2))                          # [C, H_kv, d] view
+    return out[0], out[1]
 
 
 def _branch_q_begin(inp) -> List[int]:
