@@ -28,6 +28,7 @@ EXPORTED = (
     "gqa_attn_create", "gqa_attn_forward", "gqa_attn_destroy", "gqa_attn_last_error",
     "gqa_attn_plan_stats", "gqa_attn_plan_splits", "gqa_attn_enable_timing",
     "gqa_attn_kernel_times", "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times",
+    "gqa_attn_forward_noalloc",
 )
 
 
@@ -72,6 +73,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gqa_attn_create.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(P)]
     lib.gqa_attn_forward.argtypes = [P, VP, VP, VP, I32, VP, VP, VP, I32, I32, I32P, I32P, I32, I32P, I32P,
                                      I32P, I32P, I32, VP, VP, VP]
+    lib.gqa_attn_forward_noalloc.argtypes = lib.gqa_attn_forward.argtypes
     lib.gqa_attn_destroy.argtypes = [P]
     lib.gqa_attn_last_error.restype = ctypes.c_char_p
     lib.gqa_attn_plan_stats.argtypes = [P, ctypes.POINTER(PlanStats)]
@@ -86,7 +88,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gqa_attn_append_times.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]
     for name in ("gqa_attn_create", "gqa_attn_forward", "gqa_attn_destroy", "gqa_attn_plan_stats",
                  "gqa_attn_plan_splits", "gqa_attn_enable_timing", "gqa_attn_kernel_times",
-                 "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times"):
+                 "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times",
+                 "gqa_attn_forward_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib

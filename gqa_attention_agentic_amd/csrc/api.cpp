@@ -17,7 +17,8 @@
 // so), and the partial workspace. A buffer that a forward under HIP graph
 // capture referenced is never rewritten with other contents nor freed before
 // the handle is destroyed, so a captured graph stays valid after later
-// forwards with other metadata.
+// forwards with other metadata. The no-allocation variant keeps the same
+// three regions in the library's static per-device scratch (scratch.hip).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -25,6 +26,7 @@
 #include <cmath>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -71,8 +73,12 @@ struct PlanLayout {
   size_t wide = 0, narrow = 0, wide_bins = 0, narrow_bins = 0, tok_rec = 0, combs = 0, bytes = 0;
 };
 
-// Every plan a handle builds gets a process-unique id.
+// Every plan a handle builds gets a process-unique id, so that the
+// no-allocation scratch of a device knows whose plan it holds.
 std::atomic<uint64_t> g_next_plan_id{1};
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t g_scratch_plan[kMaxDevices];   // plan id whose serialisation the device's scratch holds (0: none)
 
 }  // namespace
 
@@ -86,17 +92,20 @@ struct gqa_attn {
   gqa::Plan plan;
   bool have_plan = false;
   uint64_t plan_id = 0;
-  // device copy of plan `d_plan_id` and its pinned staging
+  // device copy of plan `d_plan_id`, its pinned staging, and a pageable
+  // serialisation for the no-allocation path
   DevBuf d_plan;
   uint64_t d_plan_id = 0;
   char* h_staging = nullptr;
   size_t h_staging_cap = 0;
   hipEvent_t staging_free = nullptr;   // recorded after the last staging -> device copy
+  std::vector<char> h_pageable;
   // arrival counters (one per query token and KV head) and partial workspace
   // ((m, l) rows, then O rows)
   DevBuf d_counters;
   DevBuf d_work;
   std::vector<char*> retired;          // buffers a captured graph may still read
+  void* scratch = nullptr;             // this device's no-allocation scratch
   // K/V append: per-row (branch, position) list on the device, and a ring
   // of pinned staging slots, each with the event after which it may be
   // rewritten (the host waits only for the upload of four calls back)
@@ -373,7 +382,9 @@ gqa_status launch_forward(gqa_attn* h, const ForwardArgs& f, const gqa::Plan& Q,
   return GQA_OK;
 }
 
-gqa_status forward_impl(gqa_attn* h, const ForwardArgs& f) {
+enum class Mode { kOwned, kScratch };
+
+gqa_status forward_impl(gqa_attn* h, const ForwardArgs& f, Mode mode) {
   if (!h) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
   gqa::PlanInput in;
   gqa_status s = make_input(&h->p, f.n_groups, f.group_shared_start, f.group_shared_len, f.n_branches,
@@ -437,12 +448,32 @@ gqa_status forward_impl(gqa_attn* h, const ForwardArgs& f) {
   const char* under_capture =
       "under HIP graph capture a forward must reuse the plan and buffers of an earlier forward with the "
       "same metadata: make one outside capture first";
-  if (h->p.workspace_bytes_cap > 0 && cnt_need + work_need > (size_t)h->p.workspace_bytes_cap)
-    return fail(GQA_ERR_NO_MEMORY, "partial workspace of " + std::to_string(cnt_need + work_need) +
-                                       " bytes exceeds workspace_bytes_cap");
-  if (capturing && (!same || h->d_plan_id != h->plan_id || cnt_need > h->d_counters.cap ||
-                    work_need > h->d_work.cap || (P.concurrent && !h->side)))
-    return fail(GQA_ERR_INVALID_ARG, under_capture);
+  size_t plan_off = 0, work_off = 0;   // scratch mode: offsets of the plan and the partials
+  if (mode == Mode::kOwned) {
+    if (h->p.workspace_bytes_cap > 0 && cnt_need + work_need > (size_t)h->p.workspace_bytes_cap)
+      return fail(GQA_ERR_NO_MEMORY, "partial workspace of " + std::to_string(cnt_need + work_need) +
+                                         " bytes exceeds workspace_bytes_cap");
+    if (capturing && (!same || h->d_plan_id != h->plan_id || cnt_need > h->d_counters.cap ||
+                      work_need > h->d_work.cap || (P.concurrent && !h->side)))
+      return fail(GQA_ERR_INVALID_ARG, under_capture);
+  } else {
+    if (!h->scratch) return fail(GQA_ERR_HIP, "the no-allocation scratch of this device is not set up");
+    if (cnt_need > gqa::kScratchCounterBytes)
+      return fail(GQA_ERR_NO_MEMORY, "arrival counters of " + std::to_string(cnt_need) +
+                                         " bytes exceed the scratch's counter region of " +
+                                         std::to_string(gqa::kScratchCounterBytes));
+    plan_off = gqa::kScratchCounterBytes;
+    work_off = plan_off + align_up(L.bytes, 256);
+    if (work_off + work_need > gqa::kScratchBytes)
+      return fail(GQA_ERR_NO_MEMORY, "this forward needs " + std::to_string(work_off + work_need) +
+                                         " bytes of scratch (plan " + std::to_string(L.bytes) + ", partials " +
+                                         std::to_string(work_need) + "); the no-allocation scratch holds " +
+                                         std::to_string(gqa::kScratchBytes));
+    if (capturing) {
+      std::lock_guard<std::mutex> lock(g_scratch_mu);
+      if (!same || g_scratch_plan[h->device] != h->plan_id) return fail(GQA_ERR_INVALID_ARG, under_capture);
+    }
+  }
 
   // The host plan is committed; from here on a failure leaves it cached
   // (it is valid) and the device copy marked stale.
@@ -453,55 +484,77 @@ gqa_status forward_impl(gqa_attn* h, const ForwardArgs& f) {
     h->plan_id = g_next_plan_id.fetch_add(1);
   }
   const gqa::Plan& Q = h->plan;
-  const bool upload = h->d_plan_id != h->plan_id;
+  const bool upload = mode == Mode::kOwned ? h->d_plan_id != h->plan_id : false;
 
   DevRegions R{};
   bool clear_counters = false;
-  // Every allocation before the first launch.
-  s = ensure_buf(h, h->d_counters, cnt_need, false, "counter", &clear_counters);
-  if (s == GQA_OK) s = ensure_buf(h, h->d_work, work_need, false, "workspace", nullptr);
-  if (s == GQA_OK && upload) s = ensure_buf(h, h->d_plan, L.bytes, true, "device plan", nullptr);
-  if (s != GQA_OK) return s;
-  if (upload) {
-    if (h->staging_free) {   // the staging buffer may still feed the previous copy
-      e = hipEventSynchronize(h->staging_free);
-      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    } else {
-      e = hipEventCreateWithFlags(&h->staging_free, hipEventDisableTiming);
-      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  if (mode == Mode::kOwned) {
+    // Every allocation before the first launch.
+    s = ensure_buf(h, h->d_counters, cnt_need, false, "counter", &clear_counters);
+    if (s == GQA_OK) s = ensure_buf(h, h->d_work, work_need, false, "workspace", nullptr);
+    if (s == GQA_OK && upload) s = ensure_buf(h, h->d_plan, L.bytes, true, "device plan", nullptr);
+    if (s != GQA_OK) return s;
+    if (upload) {
+      if (h->staging_free) {   // the staging buffer may still feed the previous copy
+        e = hipEventSynchronize(h->staging_free);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      } else {
+        e = hipEventCreateWithFlags(&h->staging_free, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      }
+      if (L.bytes > h->h_staging_cap) {
+        if (h->h_staging) hipHostFree(h->h_staging);
+        h->h_staging = nullptr;
+        h->h_staging_cap = 0;
+        e = hipHostMalloc((void**)&h->h_staging, L.bytes, hipHostMallocDefault);
+        if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "pinned plan staging allocation failed");
+        h->h_staging_cap = L.bytes;
+      }
     }
-    if (L.bytes > h->h_staging_cap) {
-      if (h->h_staging) hipHostFree(h->h_staging);
-      h->h_staging = nullptr;
-      h->h_staging_cap = 0;
-      e = hipHostMalloc((void**)&h->h_staging, L.bytes, hipHostMallocDefault);
-      if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "pinned plan staging allocation failed");
-      h->h_staging_cap = L.bytes;
+    if (Q.concurrent && !h->side) {
+      e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "side stream creation");
     }
+    // Launches.
+    if (clear_counters) {
+      e = gqa::launch_zero_i32((int32_t*)h->d_counters.p, (int64_t)(h->d_counters.cap / sizeof(int32_t)), st);
+      if (e != hipSuccess) return hip_fail(e, "counter clear");
+    }
+    if (upload) {
+      serialise_plan(Q, L, h->h_staging);
+      e = hipMemcpyAsync(h->d_plan.p, h->h_staging, L.bytes, hipMemcpyHostToDevice, st);
+      if (e == hipSuccess) e = hipEventRecord(h->staging_free, st);
+      if (e != hipSuccess) return hip_fail(e, "plan upload");
+      h->d_plan_id = h->plan_id;
+    }
+    if (capturing) h->d_plan.captured = h->d_counters.captured = h->d_work.captured = true;
+    R.plan = h->d_plan.p;
+    R.counters = (int32_t*)h->d_counters.p;
+    R.work = h->d_work.p;
+  } else {
+    char* base = (char*)h->scratch;
+    {
+      std::lock_guard<std::mutex> lock(g_scratch_mu);
+      if (g_scratch_plan[h->device] != h->plan_id) {
+        // From pageable host memory: the copy is staged before the call
+        // returns, and stays ordered on the stream.
+        h->h_pageable.resize(L.bytes);
+        serialise_plan(Q, L, h->h_pageable.data());
+        e = hipMemcpyAsync(base + plan_off, h->h_pageable.data(), L.bytes, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) {
+          g_scratch_plan[h->device] = 0;
+          return hip_fail(e, "plan upload to the scratch");
+        }
+        g_scratch_plan[h->device] = h->plan_id;
+      }
+    }
+    R.plan = base + plan_off;
+    R.counters = (int32_t*)base;
+    R.work = base + work_off;
   }
-  if (Q.concurrent && !h->side) {
-    e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "side stream creation");
-  }
-  // Launches.
-  if (clear_counters) {
-    e = gqa::launch_zero_i32((int32_t*)h->d_counters.p, (int64_t)(h->d_counters.cap / sizeof(int32_t)), st);
-    if (e != hipSuccess) return hip_fail(e, "counter clear");
-  }
-  if (upload) {
-    serialise_plan(Q, L, h->h_staging);
-    e = hipMemcpyAsync(h->d_plan.p, h->h_staging, L.bytes, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipEventRecord(h->staging_free, st);
-    if (e != hipSuccess) return hip_fail(e, "plan upload");
-    h->d_plan_id = h->plan_id;
-  }
-  if (capturing) h->d_plan.captured = h->d_counters.captured = h->d_work.captured = true;
-  R.plan = h->d_plan.p;
-  R.counters = (int32_t*)h->d_counters.p;
-  R.work = h->d_work.p;
-  TimerSlot* tm = (h->timing && !capturing) ? next_timer(h) : nullptr;
+  TimerSlot* tm = (h->timing && !capturing && mode == Mode::kOwned) ? next_timer(h) : nullptr;
   return launch_forward(h, f, Q, L, R, st, tm, h->side != nullptr);
 }
 
@@ -519,6 +572,7 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GQA_ERR_UNSUPPORTED, "device index out of range");
   int ncu = 0;
   e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
@@ -533,6 +587,13 @@ gqa_status gqa_attn_create(const gqa_attn_params* p, gqa_attn** out) {
     delete h;
     return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   }
+  // The device's no-allocation scratch: its address, looked up once per
+  // device with the device current (and its counters cleared).
+  e = gqa::scratch_setup(dev, &h->scratch);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "scratch set-up");
+  }
   *out = h;
   return GQA_OK;
 }
@@ -541,6 +602,10 @@ gqa_status gqa_attn_destroy(gqa_attn* h) {
   if (!h) return GQA_OK;
   hipSetDevice(h->device);
   hipDeviceSynchronize();
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (h->plan_id && g_scratch_plan[h->device] == h->plan_id) g_scratch_plan[h->device] = 0;
+  }
   for (DevBuf* b : {&h->d_plan, &h->d_counters, &h->d_work})
     if (b->p) hipFree(b->p);
   for (char* p : h->retired) hipFree(p);
@@ -574,9 +639,21 @@ gqa_status gqa_attn_forward(gqa_attn* h, const void* q, const void* k_shared, co
   const ForwardArgs f{q, k_shared, v_shared, n_shared_tokens, k_pages, v_pages, page_table, max_pages_per_branch,
                       n_groups, group_shared_start, group_shared_len, n_branches, branch_group, branch_q_len,
                       branch_private_len, splits_override, causal, o, lse, stream};
-  return forward_impl(h, f);
+  return forward_impl(h, f, Mode::kOwned);
 }
 
+gqa_status gqa_attn_forward_noalloc(gqa_attn* h, const void* q, const void* k_shared, const void* v_shared,
+                                    int32_t n_shared_tokens, const void* k_pages, const void* v_pages,
+                                    const int32_t* page_table, int32_t max_pages_per_branch, int32_t n_groups,
+                                    const int32_t* group_shared_start, const int32_t* group_shared_len,
+                                    int32_t n_branches, const int32_t* branch_group, const int32_t* branch_q_len,
+                                    const int32_t* branch_private_len, const int32_t* splits_override,
+                                    int32_t causal, void* o, float* lse, void* stream) {
+  const ForwardArgs f{q, k_shared, v_shared, n_shared_tokens, k_pages, v_pages, page_table, max_pages_per_branch,
+                      n_groups, group_shared_start, group_shared_len, n_branches, branch_group, branch_q_len,
+                      branch_private_len, splits_override, causal, o, lse, stream};
+  return forward_impl(h, f, Mode::kScratch);
+}
 
 namespace {
 

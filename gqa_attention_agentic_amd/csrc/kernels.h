@@ -58,6 +58,17 @@ hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, int max_part
 // Zero fill of n int32 values (fill.hip): the arrival counters.
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 
+// Static device scratch of the forwards that allocate nothing (scratch.hip):
+// kScratchBytes per device, starting with kScratchCounterBytes of arrival
+// counters (zero between forwards), then the plan and the partials.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchCounterBytes = size_t(1) << 20;
+
+// Device address of the scratch on `device` (which must be current): looked
+// up once per device with hipGetSymbolAddress, its counter region cleared
+// the first time (a synchronous fill on the null stream).
+hipError_t scratch_setup(int device, void** ptr);
+
 // Append of new K and V rows to branches' private pages (append.hip).
 struct AppendArgs {
   const void* k_new;        // [n_rows, H_kv, d]

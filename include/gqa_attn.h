@@ -150,6 +150,50 @@ gqa_status gqa_attn_forward(gqa_attn* h,
                             void* o, float* lse,
                             void* stream);
 
+/* The same forward, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Arguments, semantics and errors are those of
+ * gqa_attn_forward; the differences are where its scratch lives and what
+ * that costs:
+ *  - The plan, the arrival counters and the split-KV partials go to a
+ *    static device array of the library (64 MiB per GPU, 1 MiB of it
+ *    counters), one per GPU, held until the process ends; its address is
+ *    looked up by gqa_attn_create. The call makes no hipMalloc / hipFree /
+ *    hipHostMalloc and no allocating library call; the host planner uses
+ *    ordinary heap memory when the metadata changes.
+ *  - A forward whose plan and partials do not fit returns
+ *    GQA_ERR_NO_MEMORY before any launch (n_q_tokens x H_kv counters must
+ *    fit 1 MiB; plan + partial rows x (d + 2) x 4 bytes the rest). The
+ *    fan-out and decode workloads fit; a long prefill split into many
+ *    shards does not -- use gqa_attn_forward for it.
+ *  - Every call on one GPU, from any handle, shares that GPU's array, which
+ *    keeps the last call's plan and partials: calls that overlap on one GPU
+ *    (different streams, or different host threads without ordering) race.
+ *    The counters are zero between calls. A plan is uploaded (a pageable
+ *    host-to-device copy on `stream`) when the array holds another one.
+ *  - Under HIP graph capture the call must find its own plan in the array
+ *    (the same call made once outside capture, with nothing in between
+ *    replacing it); a replay is valid only while no call with other
+ *    metadata has replaced the array's plan since.
+ *  - The two attention kernels run side by side only if the handle already
+ *    has its side stream (made by an earlier gqa_attn_forward that needed
+ *    it); otherwise one after the other on `stream`, with the same result.
+ *  - No timing events are recorded. */
+gqa_status gqa_attn_forward_noalloc(gqa_attn* h,
+                                    const void* q,
+                                    const void* k_shared, const void* v_shared,
+                                    int32_t n_shared_tokens,
+                                    const void* k_pages, const void* v_pages,
+                                    const int32_t* page_table, int32_t max_pages_per_branch,
+                                    int32_t n_groups, const int32_t* group_shared_start,
+                                    const int32_t* group_shared_len,
+                                    int32_t n_branches, const int32_t* branch_group,
+                                    const int32_t* branch_q_len, const int32_t* branch_private_len,
+                                    const int32_t* splits_override,
+                                    int32_t causal,
+                                    void* o, float* lse,
+                                    void* stream);
+
 /* Append new K and V rows to branches' private pages: the step before a
  * forward that attends to them. A branch's context is its group's shared
  * prefix (referenced, never copied) followed by its private pages, filled

@@ -1,0 +1,148 @@
+"""gqa_attn_forward_noalloc against gqa_attn_forward, through the C ABI.
+
+The no-allocation entry point runs the same kernels with its plan, arrival
+counters and partials in the library's static per-device scratch. On the
+same inputs it must give the existing entry point's result -- bit for bit,
+and so within the parity tolerance -- on two calls in a row, the second with
+a smaller input; and a forward that does not fit the scratch must be refused
+before any launch.
+"""
+
+import ctypes
+
+import pytest
+import torch
+
+from gqa_attention_agentic_amd import _lib
+from workload import custom, generate, get_workload
+
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 3.0
+
+
+def _call(h, entry, inp, causal, out, lse, splits=None):
+    ptr = lambda t: t.data_ptr() if t.numel() > 0 else None
+    ia = _lib.int_array
+    ng, nb = len(inp.group_shared_start), len(inp.branch_group)
+    fn = getattr(h.lib, entry)
+    st = fn(h._h, ptr(inp.q), ptr(inp.k_shared), ptr(inp.v_shared), inp.k_shared.shape[1], ptr(inp.k_pages),
+            ptr(inp.v_pages), ptr(inp.page_table), inp.page_table.shape[1], ng, ia(inp.group_shared_start),
+            ia(inp.group_shared_len), nb, ia(inp.branch_group), ia(inp.branch_q_len),
+            ia(inp.branch_private_len), ia(splits) if splits is not None else None, int(causal), ptr(out),
+            ptr(lse), torch.cuda.current_stream().cuda_stream)
+    return st, h.lib.gqa_attn_last_error().decode()
+
+
+def _both(w, inp, h_ref, h_na):
+    """(reference O, LSE) from gqa_attn_forward and (O, LSE) from the
+    no-allocation entry point, on fresh outputs filled with a sentinel."""
+    res = []
+    for h, entry in ((h_ref, "gqa_attn_forward"), (h_na, "gqa_attn_forward_noalloc")):
+        out = torch.full_like(inp.q, SENTINEL)
+        lse = torch.full((inp.q.shape[0], w.num_q_heads), SENTINEL, dtype=torch.float32, device="cuda")
+        st, msg = _call(h, entry, inp, w.causal, out, lse, splits=w.splits)
+        assert st == _lib.GQA_OK, (entry, st, msg)
+        torch.cuda.synchronize()
+        res.append((out, lse))
+    return res
+
+
+def _check(w, inp, ref, got, label):
+    (o_ref, l_ref), (o, l) = ref, got
+    H.say(f"  {label}: bitwise {torch.equal(o, o_ref) and torch.equal(l, l_ref)}")
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref), label
+    orc = H.oracle_rows(w, inp)
+    H.compare(w, o, l, orc[0], orc[1], orc[2], label=label)
+
+
+# (larger, smaller) pairs; the first of each pair exercises split partials and
+# the in-launch combination, the second shrinks every size.
+PAIRS = {
+    "fanout": (custom("na_fanout_big", shared=(1500,), branches=((0, 5, 37), (0, 7, 50), (0, 20, 100)),
+                      seed=201, splits=[4, 2, 2, 2]),
+               custom("na_fanout_small", shared=(300,), branches=((0, 2, 9), (0, 3, 20)), seed=202,
+                      splits=[2, 1, 1])),
+    "decode": (custom("na_decode_big", shared=(6000,), branches=((0, 1, 0),), causal=False, seed=203,
+                      splits=[24, 0]),
+               custom("na_decode_small", shared=(900,), branches=((0, 1, 0),), causal=False, seed=204,
+                      splits=[4, 0])),
+    "mixed": (custom("na_mixed_big", shared=(0, 700),
+                     branches=((0, 1, 100), (0, 1, 2500), (0, 1, 900)) + tuple((1, 3, 40) for _ in range(5)),
+                     seed=205),
+              custom("na_mixed_small", shared=(0, 200), branches=((0, 1, 50), (1, 2, 10), (1, 2, 12)),
+                     seed=206)),
+}
+
+
+@pytest.mark.parametrize("pair", sorted(PAIRS))
+def test_noalloc_matches_forward_twice_second_smaller(pair):
+    big, small = PAIRS[pair]
+    h_ref, h_na = H.handle_for(big), H.handle_for(big)
+    for w in (big, small):
+        inp = generate(w, "cuda")
+        ref, got = _both(w, inp, h_ref, h_na)
+        _check(w, inp, ref, got, f"{pair}: {w.name}")
+    h_ref.close()
+    h_na.close()
+
+
+def test_noalloc_full_size_decode_and_fanout():
+    """The two workloads the scratch is sized for, at full size: the 8k
+    decode (32 shards) and the 8-agent fan-out over 32k (library splits)."""
+    for name in ("decode_8k", "fanout_8x20_32k"):
+        w = get_workload(name)
+        inp = generate(w, "cuda")
+        h_ref, h_na = H.handle_for(w), H.handle_for(w)
+        ref, got = _both(w, inp, h_ref, h_na)
+        H.say(f"  {name}: bitwise {torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])}")
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), name
+        h_ref.close()
+        h_na.close()
+
+
+def test_noalloc_two_handles_share_the_scratch():
+    """Two handles alternating on one GPU: each call finds the other's plan in
+    the scratch and uploads its own; results stay bit-identical."""
+    wa, wb = PAIRS["fanout"][0], PAIRS["decode"][0]
+    ia, ib = generate(wa, "cuda"), generate(wb, "cuda")
+    ha, hb, hr = H.handle_for(wa), H.handle_for(wb), H.handle_for(wa)
+    refs = {}
+    for w, inp in ((wa, ia), (wb, ib)):
+        refs[w.name] = _both(w, inp, hr, hr)[0]
+    for rep in range(3):
+        for w, inp, h in ((wa, ia, ha), (wb, ib, hb)):
+            out = torch.full_like(inp.q, SENTINEL)
+            lse = torch.full((inp.q.shape[0], w.num_q_heads), SENTINEL, dtype=torch.float32, device="cuda")
+            st, msg = _call(h, "gqa_attn_forward_noalloc", inp, w.causal, out, lse, splits=w.splits)
+            assert st == _lib.GQA_OK, msg
+            torch.cuda.synchronize()
+            assert torch.equal(out, refs[w.name][0]) and torch.equal(lse, refs[w.name][1]), (rep, w.name)
+    for h in (ha, hb, hr):
+        h.close()
+
+
+def test_noalloc_refuses_what_does_not_fit():
+    """A prefill of 4096 tokens in 16 shards needs ~280 MB of partials: the
+    call returns GQA_ERR_NO_MEMORY naming the scratch size, launches nothing,
+    and the handle then still serves a forward that fits."""
+    w = custom("na_too_big", shared=(4096,), branches=((0, 4096, 0),), seed=207, splits=[16, 0])
+    inp = generate(w, "cuda")
+    h = H.handle_for(w)
+    out = torch.full_like(inp.q, SENTINEL)
+    lse = torch.full((inp.q.shape[0], w.num_q_heads), SENTINEL, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    st, msg = _call(h, "gqa_attn_forward_noalloc", inp, w.causal, out, lse, splits=w.splits)
+    H.say(f"  too big: status {st}, '{msg}'")
+    assert st == _lib.GQA_ERR_NO_MEMORY and "scratch" in msg, (st, msg)
+    torch.cuda.synchronize()
+    assert bool((out == SENTINEL).all()) and bool((lse == SENTINEL).all())
+    small = PAIRS["fanout"][1]
+    si = generate(small, "cuda")
+    h2 = H.handle_for(small)
+    ref, got = _both(small, si, h2, h)
+    _check(small, si, ref, got, "after the refusal")
+    h.close()
+    h2.close()
