@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 from . import _lib
 from ._lib import GqaError, load  # noqa: F401
 
-__all__ = ["GqaAttention", "plan_host", "load", "GqaError"]
+__all__ = ["GqaAttention", "plan_host", "probe_mfma_bf16", "probe_read", "load", "GqaError"]
 
 _DTYPES = {"bf16": _lib.GQA_BF16, "fp32": _lib.GQA_FP32}
 
@@ -156,6 +156,18 @@ class GqaAttention:
         _lib.check(self.lib.gqa_attn_kernel_times(self._h, ctypes.byref(a), ctypes.byref(m), ctypes.byref(n)))
         return a.value, m.value, n.value
 
+    def kernel_times_list(self):
+        """Per timed forward since timing was enabled: a list of (attention
+        ms, merge ms), in issue order; clears the records."""
+        n = ctypes.c_int64()
+        st = self.lib.gqa_attn_kernel_times_list(self._h, None, None, 0, ctypes.byref(n))
+        if st != _lib.GQA_OK and n.value == 0:
+            _lib.check(st)
+        cap = max(1, n.value)
+        a, m = (ctypes.c_double * cap)(), (ctypes.c_double * cap)()
+        _lib.check(self.lib.gqa_attn_kernel_times_list(self._h, a, m, cap, ctypes.byref(n)))
+        return [(a[k], m[k]) for k in range(n.value)]
+
     def append_times(self):
         """(append kernel ms, appends) summed since timing was enabled."""
         m, n = ctypes.c_double(), ctypes.c_int64()
@@ -195,3 +207,24 @@ def plan_host(num_q_heads, num_kv_heads, head_dim, page_size, group_shared_start
     _lib.check(lib.gqa_attn_plan_host(*args, items, n.value, ctypes.byref(n), spl, ctypes.byref(stats)))
     flat = list(items)
     return ([tuple(flat[9 * i:9 * i + 9]) for i in range(n.value)], list(spl)[: ng + nb], stats.as_dict())
+
+
+def probe_mfma_bf16(waves_per_simd: int = 2, iters: int = 2048, reps: int = 20):
+    """Achievable bf16 MFMA rate (include/gqa_probe.h): (median TFLOP/s,
+    median ms per launch)."""
+    lib = load()
+    t, ms = ctypes.c_double(), ctypes.c_double()
+    _lib.check(lib.gqa_probe_mfma_bf16(int(waves_per_simd), int(iters), int(reps), ctypes.byref(t), ctypes.byref(ms)))
+    return t.value, ms.value
+
+
+def probe_read(buf, bytes_per_copy: int, n_copies: int, reps: int = 20):
+    """Achievable streaming-read rate over copy k % n_copies of the device
+    tensor `buf` (include/gqa_probe.h): (median GB/s, median us per launch)."""
+    lib = load()
+    if buf.numel() * buf.element_size() < bytes_per_copy * n_copies:
+        raise ValueError("buf is smaller than n_copies x bytes_per_copy")
+    g, us = ctypes.c_double(), ctypes.c_double()
+    _lib.check(lib.gqa_probe_read(buf.data_ptr(), int(bytes_per_copy), int(n_copies), int(reps), ctypes.byref(g),
+                                  ctypes.byref(us)))
+    return g.value, us.value

@@ -28,8 +28,10 @@ EXPORTED = (
     "gqa_attn_create", "gqa_attn_forward", "gqa_attn_destroy", "gqa_attn_last_error",
     "gqa_attn_plan_stats", "gqa_attn_plan_splits", "gqa_attn_enable_timing",
     "gqa_attn_kernel_times", "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times",
-    "gqa_attn_forward_noalloc",
+    "gqa_attn_forward_noalloc", "gqa_attn_kernel_times_list",
 )
+# Every symbol include/gqa_probe.h declares (measurement only).
+PROBES = ("gqa_probe_mfma_bf16", "gqa_probe_read")
 
 
 class Params(ctypes.Structure):
@@ -74,6 +76,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gqa_attn_forward.argtypes = [P, VP, VP, VP, I32, VP, VP, VP, I32, I32, I32P, I32P, I32, I32P, I32P,
                                      I32P, I32P, I32, VP, VP, VP]
     lib.gqa_attn_forward_noalloc.argtypes = lib.gqa_attn_forward.argtypes
+    DP = ctypes.POINTER(ctypes.c_double)
+    lib.gqa_attn_kernel_times_list.argtypes = [P, DP, DP, I64, ctypes.POINTER(I64)]
+    lib.gqa_probe_mfma_bf16.argtypes = [I32, I32, I32, DP, DP]
+    lib.gqa_probe_read.argtypes = [VP, I64, I32, I32, DP, DP]
     lib.gqa_attn_destroy.argtypes = [P]
     lib.gqa_attn_last_error.restype = ctypes.c_char_p
     lib.gqa_attn_plan_stats.argtypes = [P, ctypes.POINTER(PlanStats)]
@@ -89,7 +95,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("gqa_attn_create", "gqa_attn_forward", "gqa_attn_destroy", "gqa_attn_plan_stats",
                  "gqa_attn_plan_splits", "gqa_attn_enable_timing", "gqa_attn_kernel_times",
                  "gqa_attn_plan_host", "gqa_attn_append_kv", "gqa_attn_append_times",
-                 "gqa_attn_forward_noalloc"):
+                 "gqa_attn_forward_noalloc", "gqa_attn_kernel_times_list", "gqa_probe_mfma_bf16",
+                 "gqa_probe_read"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib

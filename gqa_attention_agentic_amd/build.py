@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgqa_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attention.hip", "append.hip", "fill.hip", "scratch.hip", "api.cpp", "plan.cpp"]
+SOURCES = ["attention.hip", "append.hip", "fill.hip", "scratch.hip", "probe.hip", "api.cpp", "plan.cpp"]
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Kernels run with the IEEE mode bit off: max/min then need no NaN-quieting
 # canonicalisation of their inputs. The kernels never produce NaN themselves

@@ -31,6 +31,7 @@
 #include <vector>
 
 #include "../../include/gqa_attn.h"
+#include "../../include/gqa_probe.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -813,42 +814,77 @@ gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable) {
   return GQA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Attention and merge milliseconds of the timed forward `t` (when the two
+// attention kernels ran side by side: the span from the earlier start to
+// the later end).
+gqa_status forward_times(TimerSlot& t, double* attn, double* merge) {
+  const bool used[3] = {t.wide, t.narrow, t.merged};
+  for (int j = 0; j < 3; ++j) {
+    if (!used[j]) continue;
+    hipError_t e = hipEventSynchronize(t.ev[2 * j + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  *attn = *merge = 0.0;
+  for (int j = 0; j < 3; ++j) {
+    if (!used[j] || (t.concurrent && j == 1)) continue;
+    float ms = 0.f;
+    hipError_t e;
+    if (t.concurrent && j == 0) {
+      float best = 0.f;
+      for (int s0 : {0, 2})
+        for (int s1 : {1, 3}) {
+          e = hipEventElapsedTime(&ms, t.ev[s0], t.ev[s1]);
+          if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+          best = std::max(best, ms);
+        }
+      ms = best;
+    } else {
+      e = hipEventElapsedTime(&ms, t.ev[2 * j], t.ev[2 * j + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    }
+    (j < 2 ? *attn : *merge) += ms;
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms, int64_t* n_forwards) {
   if (!h || !attn_ms || !merge_ms || !n_forwards) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
   double at = 0.0, mg = 0.0;
   for (size_t k = 0; k < h->timers_used; ++k) {
-    TimerSlot& t = h->timers[k];
-    const bool used[3] = {t.wide, t.narrow, t.merged};
-    for (int j = 0; j < 3; ++j) {
-      if (!used[j]) continue;
-      hipError_t e = hipEventSynchronize(t.ev[2 * j + 1]);
-      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    }
-    for (int j = 0; j < 3; ++j) {
-      if (!used[j] || (t.concurrent && j == 1)) continue;
-      float ms = 0.f;
-      hipError_t e;
-      if (t.concurrent && j == 0) {
-        // Side by side: the span from the earlier start to the later end,
-        // i.e. the largest (end - start) over the four pairs.
-        float best = 0.f;
-        for (int s0 : {0, 2})
-          for (int s1 : {1, 3}) {
-            e = hipEventElapsedTime(&ms, t.ev[s0], t.ev[s1]);
-            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-            best = std::max(best, ms);
-          }
-        ms = best;
-      } else {
-        e = hipEventElapsedTime(&ms, t.ev[2 * j], t.ev[2 * j + 1]);
-        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-      }
-      (j < 2 ? at : mg) += ms;
-    }
+    double a = 0.0, m = 0.0;
+    gqa_status s = forward_times(h->timers[k], &a, &m);
+    if (s != GQA_OK) return s;
+    at += a;
+    mg += m;
   }
   *attn_ms = at;
   *merge_ms = mg;
   *n_forwards = (int64_t)h->timers_used;
+  h->timers_used = 0;
+  return GQA_OK;
+}
+
+gqa_status gqa_attn_kernel_times_list(gqa_attn* h, double* attn_ms, double* merge_ms, int64_t cap,
+                                      int64_t* n_forwards) {
+  if (!h || !n_forwards) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  const int64_t n = (int64_t)h->timers_used;
+  if (cap < n || (n > 0 && (!attn_ms || !merge_ms))) {
+    *n_forwards = n;
+    return fail(GQA_ERR_INVALID_ARG, "the arrays hold fewer entries than there are timed forwards");
+  }
+  for (int64_t k = 0; k < n; ++k) {
+    gqa_status s = forward_times(h->timers[k], &attn_ms[k], &merge_ms[k]);
+    if (s != GQA_OK) return s;
+  }
+  *n_forwards = n;
   h->timers_used = 0;
   return GQA_OK;
 }
@@ -886,6 +922,102 @@ gqa_status gqa_attn_plan_host(const gqa_attn_params* p, int32_t n_groups, const 
   }
   if (splits) std::memcpy(splits, P.api_splits.data(), sizeof(int32_t) * P.api_splits.size());
   if (stats) fill_stats(P, p->head_dim, stats);
+  return GQA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+double median(std::vector<double> v) {
+  if (v.empty()) return 0.0;
+  std::sort(v.begin(), v.end());
+  const size_t n = v.size();
+  return n % 2 ? v[n / 2] : 0.5 * (v[n / 2 - 1] + v[n / 2]);
+}
+
+// Runs `launch(k, e0, e1)` reps times on a private stream, each launch
+// bracketed by its own events; returns the per-launch milliseconds.
+template <class F>
+gqa_status time_launches(int32_t reps, F launch, std::vector<double>* ms) {
+  hipStream_t st = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreate");
+  std::vector<hipEvent_t> ev(2 * (size_t)reps, nullptr);
+  gqa_status s = GQA_OK;
+  for (auto& x : ev)
+    if (hipEventCreate(&x) != hipSuccess) s = fail(GQA_ERR_HIP, "hipEventCreate");
+  for (int32_t k = 0; s == GQA_OK && k < reps; ++k) {
+    e = launch(k, st, ev[2 * k], ev[2 * k + 1]);
+    if (e != hipSuccess) s = hip_fail(e, "probe launch");
+  }
+  if (s == GQA_OK) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) s = hip_fail(e, "hipStreamSynchronize");
+  }
+  for (int32_t k = 0; s == GQA_OK && k < reps; ++k) {
+    float x = 0.f;
+    e = hipEventElapsedTime(&x, ev[2 * k], ev[2 * k + 1]);
+    if (e != hipSuccess) s = hip_fail(e, "hipEventElapsedTime");
+    ms->push_back(x);
+  }
+  for (auto& x : ev)
+    if (x) hipEventDestroy(x);
+  hipStreamDestroy(st);
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_probe_mfma_bf16(int32_t waves_per_simd, int32_t iters, int32_t reps, double* tflops, double* ms) {
+  if (!tflops || !ms || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1 || reps < 1)
+    return fail(GQA_ERR_INVALID_ARG, "bad probe arguments");
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  // 256-thread workgroups are 4 waves, one per SIMD of a CU.
+  const int blocks = ncu * waves_per_simd;
+  float* out = nullptr;
+  e = hipMalloc((void**)&out, (size_t)blocks * 256 * sizeof(float));
+  if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "probe output allocation failed");
+  std::vector<double> t;
+  gqa_status s = time_launches(reps, [&](int32_t, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    return gqa::launch_probe_mfma(out, blocks, iters, st, e0, e1);
+  }, &t);
+  (void)hipFree(out);
+  if (s != GQA_OK) return s;
+  const double med = median(t);
+  const double flops = (double)blocks * 4 * iters * 4 * (32.0 * 32 * 16 * 2);
+  *ms = med;
+  *tflops = med > 0 ? flops / (med * 1e-3) / 1e12 : 0.0;
+  return GQA_OK;
+}
+
+gqa_status gqa_probe_read(const void* buf, int64_t bytes, int32_t n_copies, int32_t reps, double* gbps, double* us) {
+  if (!buf || !gbps || !us || bytes <= 0 || bytes % 16 || n_copies < 1 || reps < 1 ||
+      (reinterpret_cast<uintptr_t>(buf) & 15u))
+    return fail(GQA_ERR_INVALID_ARG, "bad probe arguments (16-byte aligned buffer of n_copies x bytes, bytes % 16 == 0)");
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  const int blocks = ncu * 8;
+  uint32_t* out = nullptr;
+  e = hipMalloc((void**)&out, (size_t)blocks * 256 * sizeof(uint32_t));
+  if (e != hipSuccess) return fail(GQA_ERR_NO_MEMORY, "probe output allocation failed");
+  std::vector<double> t;
+  gqa_status s = time_launches(reps, [&](int32_t k, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    const char* src = (const char*)buf + (int64_t)(k % n_copies) * bytes;
+    return gqa::launch_probe_read(src, bytes, out, blocks, st, e0, e1);
+  }, &t);
+  (void)hipFree(out);
+  if (s != GQA_OK) return s;
+  const double med = median(t);
+  *us = med * 1e3;
+  *gbps = med > 0 ? (double)bytes / (med * 1e-3) / 1e9 : 0.0;
   return GQA_OK;
 }
 

@@ -88,4 +88,10 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& p, int32_t n_rows, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);
 
+// Achievable-peak probes (probe.hip): `blocks` workgroups of 256 threads;
+// out holds one value per thread.
+hipError_t launch_probe_mfma(float* out, int blocks, int iters, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t st,
+                             hipEvent_t e0, hipEvent_t e1);
+
 }  // namespace gqa

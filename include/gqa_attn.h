@@ -272,6 +272,14 @@ gqa_status gqa_attn_enable_timing(gqa_attn* h, int32_t enable);
 gqa_status gqa_attn_kernel_times(gqa_attn* h, double* attn_ms, double* merge_ms,
                                  int64_t* n_forwards);
 
+/* The same records forward by forward: attn_ms[k] and merge_ms[k] (host
+ * arrays of at least `cap` entries) for the k-th timed forward, in issue
+ * order; *n_forwards is their number. Clears the records like
+ * gqa_attn_kernel_times. GQA_ERR_INVALID_ARG (records kept, *n_forwards
+ * set) when cap is smaller than that number. */
+gqa_status gqa_attn_kernel_times_list(gqa_attn* h, double* attn_ms, double* merge_ms, int64_t cap,
+                                      int64_t* n_forwards);
+
 /* Kernel time of the appends made while timing is enabled (events that each
  * append launch records around its own kernel, like gqa_attn_kernel_times):
  * summed milliseconds and the number of appends, then cleared. */

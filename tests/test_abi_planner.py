@@ -29,6 +29,11 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTED), declared ^ set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
+    probes = open(os.path.join(ROOT, "include", "gqa_probe.h")).read()
+    declared = set(re.findall(r"\b(gqa_probe_\w+)\s*\(", probes))
+    assert declared == set(_lib.PROBES), declared ^ set(_lib.PROBES)
+    for name in declared:
+        assert hasattr(lib, name), name
 
 
 def _expected_pairs(w):

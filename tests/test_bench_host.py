@@ -64,18 +64,28 @@ def test_more_than_one_gpu_is_refused():
 def test_roofline_bound_follows_the_ridge(name, bound):
     """The bound is the roofline side of the workload's algorithmic
     intensity (FLOP per unique byte) against the ridge of its dtype's peak;
-    achieved and frac are algorithmic work over the attention kernel time."""
+    achieved and frac are algorithmic work over T = attention + merge kernel
+    time per forward, frac_attention over the attention launch alone, and
+    frac_of_achievable over the probe-measured ceiling of the same kind."""
     w = get_workload(name)
-    res = {"attn_kernel_ms": 0.5}
-    r = bench.roofline_of(w, res, traffic=123)
+    res = {"attn_kernel_ms": 0.4, "kernel_ms": 0.5, "timed_forwards": 50}
+    ach = {"mfma_bf16_tflops": 2000.0, "hbm_read_gbps": 5000.0}
+    r = bench.roofline_of(w, res, traffic=123, achievable=ach)
     assert r["bound"] == bound and r["traffic"] == 123
     if bound == "mfma":
-        assert r["achieved"] == pytest.approx(w.flops() / 0.5e-3 / 1e12)
+        work, scale = w.flops(), 1e12
         assert r["peak"] == (bench.PEAK_BF16_TFLOPS if w.dtype == "bf16" else bench.PEAK_FP32_TFLOPS)
     else:
-        assert r["achieved"] == pytest.approx((w.kv_bytes() + w.io_bytes()) / 0.5e-3 / 1e9)
+        work, scale = w.kv_bytes() + w.io_bytes(), 1e9
         assert r["peak"] == bench.PEAK_HBM_GBPS
+    assert r["achieved"] == pytest.approx(work / 0.5e-3 / scale)
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    assert r["frac_attention"] == pytest.approx(work / 0.4e-3 / scale / r["peak"])
+    if w.dtype == "bf16" or bound == "hbm":
+        key = "mfma_bf16_tflops" if bound == "mfma" else "hbm_read_gbps"
+        assert r["frac_of_achievable"] == pytest.approx(r["achieved"] / ach[key])
+    else:
+        assert "frac_of_achievable" not in r
 
 
 def test_kernel_summary_separates_the_last_calls(tmp_path):
