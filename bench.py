@@ -457,6 +457,9 @@ def kernel_summary(csv_path: str, last: int):
 
     by = {}
     for name, s, e in read_kernel_trace(csv_path):
+        if "gqa::" not in name:
+            continue   # the library's kernels only (input generation and copies are left out)
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0].replace("gqa::", "")
         by.setdefault(name, []).append((e - s) / 1e3)
     print(f"| kernel | calls | average us (all calls) | average us (last {last} calls) | median us (last {last}) | min us |")
     print("|---|---|---|---|---|---|")

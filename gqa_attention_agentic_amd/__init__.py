@@ -190,8 +190,9 @@ def plan_host(num_q_heads, num_kv_heads, head_dim, page_size, group_shared_start
               branch_group, branch_q_len, branch_private_len, causal, splits=None, dtype="bf16"):
     """Host-only planner (no device use): returns (items, splits, stats) where
     items is a list of (unit_slot, kv, row_begin, n_rows, key_begin, key_end,
-    split, kernel, bin) tuples; kernel 0 = 128/256-row, 1 = 32-row; bin is
-    the workgroup of that kernel that runs the item."""
+    split, kernel, bin, chain) tuples; kernel 0 = 128/256-row, 1 = 32-row;
+    bin is the workgroup of that kernel that runs the item; chain bit 0: the
+    item continues the previous item's state, bit 1: it hands its state on."""
     lib = load()
     p = _lib.params(num_q_heads, num_kv_heads, head_dim, page_size, _dtype_code(dtype))
     ng, nb = len(group_shared_start), len(branch_group)
@@ -201,12 +202,12 @@ def plan_host(num_q_heads, num_kv_heads, head_dim, page_size, group_shared_start
             _lib.int_array(branch_private_len), _lib.int_array(splits), int(bool(causal)))
     n = ctypes.c_int64()
     _lib.check(lib.gqa_attn_plan_host(*args, None, 0, ctypes.byref(n), None, None))
-    items = (ctypes.c_int32 * max(9, 9 * n.value))()
+    items = (ctypes.c_int32 * max(10, 10 * n.value))()
     spl = (ctypes.c_int32 * max(1, ng + nb))()
     stats = _lib.PlanStats()
     _lib.check(lib.gqa_attn_plan_host(*args, items, n.value, ctypes.byref(n), spl, ctypes.byref(stats)))
     flat = list(items)
-    return ([tuple(flat[9 * i:9 * i + 9]) for i in range(n.value)], list(spl)[: ng + nb], stats.as_dict())
+    return ([tuple(flat[10 * i:10 * i + 10]) for i in range(n.value)], list(spl)[: ng + nb], stats.as_dict())
 
 
 def probe_mfma_bf16(waves_per_simd: int = 2, iters: int = 2048, reps: int = 20):

@@ -914,9 +914,9 @@ gqa_status gqa_attn_plan_host(const gqa_attn_params* p, int32_t n_groups, const 
       for (size_t x = 0; x < list.size(); ++x) {
         while (bins[b + 1] <= (int32_t)x) ++b;
         const gqa::WorkItem& w = list[x];
-        int32_t* r = items + 9 * k++;
+        int32_t* r = items + 10 * k++;
         r[0] = P.unit_slot[w.unit]; r[1] = w.kv; r[2] = w.row_begin; r[3] = w.n_rows;
-        r[4] = w.key_begin; r[5] = w.key_end; r[6] = w.split; r[7] = pass; r[8] = b;
+        r[4] = w.key_begin; r[5] = w.key_end; r[6] = w.split; r[7] = pass; r[8] = b; r[9] = w.chain;
       }
     }
   }

@@ -719,14 +719,14 @@ attn_wide(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const int bin_end = a.bins[blockIdx.x + 1];
+  State<C> s;   // carried from one item to the next along a chain
   for (int idx = a.bins[blockIdx.x]; idx < bin_end; ++idx) {
     // The previous item's last tile loop iteration ended with a barrier after
     // all LDS reads, so its stages may be refilled at once.
     const WorkItem it = a.items[idx];
     const int rloc = wave * 32 + i;
     const Row w = row_at(a, it, rloc);
-    State<C> s;
-    load_q<C, T, D>(a, w, it.kv, h, s);
+    if (!(it.chain & kChainContinues)) load_q<C, T, D>(a, w, it.kv, h, s);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
     const bool wave_rows = wave * 32 < it.n_rows;
@@ -753,7 +753,7 @@ attn_wide(AttnArgs a) {
       }
       __syncthreads();
     }
-    write_row<C, T, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
+    if (!(it.chain & kChainContinued)) write_row<C, T, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
   }
 }
 
@@ -1073,6 +1073,7 @@ attn_wide_dma(AttnArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const DmaLane<C> L = dma_lane<C>(wave, lane);
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
+  State<C> s;   // carried from one item to the next along a chain
   for (int idx = bin_begin; idx < bin_end; ++idx) {
     // Every wave has finished reading the previous item's ring before its
     // stages are refilled.
@@ -1086,8 +1087,10 @@ attn_wide_dma(AttnArgs a) {
     if (nt > 1) dma_tile_any<C, D>(src, L, wave, kb0 + C::BN, ke, k1, v1);
     const int rloc = wave * 32 + i;
     const Row w = row_at(a, it, rloc);
-    State<C> s;
-    load_q<C, uint16_t, D>(a, w, it.kv, h, s);
+    // A chain's later shards continue from the state the previous item left
+    // (ADR-0060, §4: the merge of two (m, l, O) states is the online
+    // softmax's own update, done here in registers).
+    if (!(it.chain & kChainContinues)) load_q<C, uint16_t, D>(a, w, it.kv, h, s);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
     const bool active = wave * 32 < it.n_rows;
@@ -1115,8 +1118,10 @@ attn_wide_dma(AttnArgs a) {
       }
     }
 #undef GQA_DMA_PAIR
-    s.l += __shfl_xor(s.l, 32);
-    write_row<C, uint16_t, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
+    if (!(it.chain & kChainContinued)) {
+      s.l += __shfl_xor(s.l, 32);   // the two half-rows' sums, once per result
+      write_row<C, uint16_t, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
+    }
   }
 }
 

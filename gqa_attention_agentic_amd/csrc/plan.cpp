@@ -66,6 +66,9 @@ double lpt_makespan(std::vector<double> cost, int slots) {
 // Fixed cost of an item in key units (descriptor and Q loads, the first
 // tile's latency, the partial write-back): about one and a half 64-key tiles.
 constexpr double kItemFixedKeys = 96.0;
+// Extra cost of each further shard of a chain (a barrier and the restart of
+// the K/V ring): a quarter of a 64-key tile.
+constexpr double kChainStepKeys = 16.0;
 constexpr int kXcds = 8;
 
 double item_cost(const WorkItem& w) { return (double)(w.key_end - w.key_begin) + kItemFixedKeys; }
@@ -89,71 +92,101 @@ double lpt_assign(const std::vector<double>& cost, const std::vector<size_t>& or
   return mk;
 }
 
-// Packs a kernel's items (sorted largest first) into at most `slots` bins,
-// one per resident workgroup, so that every workgroup starts at once and
-// runs its bin's items back to back; the hardware then never has to queue a
-// workgroup behind a long one.
+// Packs a kernel's items into at most `slots` bins, one per resident
+// workgroup, so that every workgroup starts at once and runs its bin's items
+// back to back; the hardware then never has to queue a workgroup behind a
+// long one. The unit of packing is a job: one item, or a chain (the
+// consecutive shards of one (unit, KV head, M-tile), which must run in
+// shard order in one workgroup). Jobs are placed largest first, so the tail
+// of each bin holds the short ones.
 //
 // Workgroups are dealt to the 8 XCDs of the chip round-robin by launch
-// index and each XCD has its own L2, so bin b runs on XCD b % 8. Items that
-// read the same KV range (same unit, KV head and shard; different M-tiles)
-// are kept on one XCD, so their K/V tiles are fetched into one L2 once:
-// such groups go to the least-loaded XCD, largest first, and each XCD's
-// items to its least-loaded bins. That placement is kept unless plain list
-// scheduling over all bins would finish more than 2% sooner.
+// index and each XCD has its own L2, so bin b runs on XCD b % 8. Jobs that
+// read the same KV range (same unit, KV head and shard -- for chains, the
+// same unit and KV head) are kept on one XCD, so their K/V tiles are
+// fetched into one L2 once: such groups go to the least-loaded XCD, largest
+// first, and each XCD's jobs to its least-loaded bins. That placement is
+// kept unless plain list scheduling over all bins would finish more than 2%
+// sooner.
 void bin_items(std::vector<WorkItem>* items, int slots, int n_cu, std::vector<int32_t>* bins) {
   const size_t n = items->size();
   bins->assign(1, 0);
   if (n == 0) return;
-  const int nb = (int)std::min<int64_t>((int64_t)n, std::max(1, slots));
-  std::vector<double> cost(n);
-  std::vector<size_t> order(n);
-  for (size_t i = 0; i < n; ++i) {
-    cost[i] = item_cost((*items)[i]);
-    order[i] = i;
+  // Jobs: chains keyed by (unit, KV head, M-tile), every other item alone;
+  // a job's items in shard order.
+  std::vector<std::vector<size_t>> job;
+  {
+    std::map<std::array<int32_t, 3>, size_t> chain_job;
+    for (size_t i = 0; i < n; ++i) {
+      const WorkItem& w = (*items)[i];
+      if (w.chain == 0) {
+        job.push_back({i});
+        continue;
+      }
+      auto ins = chain_job.emplace(std::array<int32_t, 3>{w.unit, w.kv, w.tile}, job.size());
+      if (ins.second) job.emplace_back();
+      job[ins.first->second].push_back(i);
+    }
+    for (auto& j : job)
+      std::sort(j.begin(), j.end(), [&](size_t a, size_t b) { return (*items)[a].split < (*items)[b].split; });
   }
-  std::vector<int> bin_of(n, 0);
+  const size_t nj = job.size();
+  const int nb = (int)std::min<int64_t>((int64_t)nj, std::max(1, slots));
+  std::vector<double> cost(nj, 0.0);
+  for (size_t j = 0; j < nj; ++j) {
+    for (size_t i : job[j]) cost[j] += (double)((*items)[i].key_end - (*items)[i].key_begin);
+    cost[j] += kItemFixedKeys + kChainStepKeys * (double)(job[j].size() - 1);
+  }
+  // Largest first; ties in a fixed order of the first item's fields.
+  std::vector<size_t> order(nj);
+  for (size_t j = 0; j < nj; ++j) order[j] = j;
+  auto key_of = [&](size_t j) {
+    const WorkItem& w = (*items)[job[j].front()];
+    return std::array<int32_t, 4>{w.unit, w.split, w.kv, w.tile};
+  };
+  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+    if (cost[a] != cost[b]) return cost[a] > cost[b];
+    return key_of(a) < key_of(b);
+  });
+  std::vector<int> bin_of(nj, 0);
   const double mk_plain = lpt_assign(cost, order, nb, &bin_of);
   if (n_cu % kXcds == 0 && nb % kXcds == 0 && nb >= 2 * kXcds) {
     const int per = nb / kXcds;
     std::map<std::array<int32_t, 3>, size_t> gid;
-    std::vector<std::vector<size_t>> members;
     std::vector<double> gcost;
-    for (size_t i = 0; i < n; ++i) {
-      const WorkItem& w = (*items)[i];
-      auto ins = gid.emplace(std::array<int32_t, 3>{w.unit, w.kv, w.split}, members.size());
-      if (ins.second) {
-        members.emplace_back();
-        gcost.push_back(0.0);
-      }
-      members[ins.first->second].push_back(i);
-      gcost[ins.first->second] += cost[i];
+    std::vector<size_t> group_of(nj);
+    for (size_t j = 0; j < nj; ++j) {
+      const WorkItem& w = (*items)[job[j].front()];
+      const std::array<int32_t, 3> k{w.unit, w.kv, w.chain ? -1 : w.split};
+      auto ins = gid.emplace(k, gcost.size());
+      if (ins.second) gcost.push_back(0.0);
+      group_of[j] = ins.first->second;
+      gcost[ins.first->second] += cost[j];
     }
-    std::vector<size_t> gorder(members.size());
+    std::vector<size_t> gorder(gcost.size());
     for (size_t g = 0; g < gorder.size(); ++g) gorder[g] = g;
     std::stable_sort(gorder.begin(), gorder.end(), [&](size_t a, size_t b) { return gcost[a] > gcost[b]; });
-    std::vector<int> xcd_of(members.size(), 0);
+    std::vector<int> xcd_of(gcost.size(), 0);
     lpt_assign(gcost, gorder, kXcds, &xcd_of);
     std::vector<std::vector<size_t>> on_xcd(kXcds);
-    for (size_t i = 0; i < n; ++i) {
-      const WorkItem& w = (*items)[i];
-      on_xcd[xcd_of[gid[std::array<int32_t, 3>{w.unit, w.kv, w.split}]]].push_back(i);   // index order = largest first
-    }
-    std::vector<int> local(n, 0);
+    for (size_t j : order) on_xcd[xcd_of[group_of[j]]].push_back(j);   // largest first
+    std::vector<int> local(nj, 0);
     double mk_xcd = 0.0;
     for (int x = 0; x < kXcds; ++x) mk_xcd = std::max(mk_xcd, lpt_assign(cost, on_xcd[x], per, &local));
     if (mk_xcd <= mk_plain * 1.02) {
       for (int x = 0; x < kXcds; ++x)
-        for (size_t i : on_xcd[x]) bin_of[i] = local[i] * kXcds + x;
+        for (size_t j : on_xcd[x]) bin_of[j] = local[j] * kXcds + x;
     }
   }
-  // Items of bin b, in the (largest-first) order they were assigned.
+  // Items of bin b: its jobs in the (largest-first) order they were
+  // assigned, each job's items in shard order.
   std::vector<int32_t> count(nb + 1, 0);
-  for (size_t i = 0; i < n; ++i) ++count[bin_of[i] + 1];
+  for (size_t j = 0; j < nj; ++j) count[bin_of[j] + 1] += (int32_t)job[j].size();
   for (int b = 0; b < nb; ++b) count[b + 1] += count[b];
   bins->assign(count.begin(), count.end());
   std::vector<WorkItem> out(n);
-  for (size_t i = 0; i < n; ++i) out[count[bin_of[i]]++] = (*items)[i];
+  for (size_t j : order)
+    for (size_t i : job[j]) out[count[bin_of[j]]++] = (*items)[i];
   *items = std::move(out);
 }
 
@@ -304,16 +337,21 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     P->units.push_back(u);
   }
 
-  // M-tiles (whole tokens: bm / G of them, so every row of a token shares
-  // one M-tile of each unit) and their causal key clamp.
+  // M-tiles (whole tokens, so every row of a token shares one M-tile of
+  // each unit) and their causal key clamp. A unit's tokens are spread evenly
+  // over the fewest tiles of at most bm / G tokens: tiles of one unit then
+  // have the same number of active waves and stream the unit's K/V tiles at
+  // the same pace, so one L2 serves all of them (a full tile next to a
+  // remnant would run behind it and fetch the shared prefix a second time).
   const int32_t nu = (int32_t)P->units.size();
   std::vector<UnitWork> uw(nu);
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
     const int64_t M = (int64_t)u.n_tok * G;
     u.bm = (M <= kNarrowRows) ? kNarrowRows : wide_rows;
-    u.tpt = u.bm / G;
-    const int32_t ntile = (int32_t)ceil_div(u.n_tok, u.tpt);
+    const int32_t cap = u.bm / G;
+    const int32_t ntile = (int32_t)ceil_div(u.n_tok, cap);
+    u.tpt = (int32_t)ceil_div(u.n_tok, ntile);
     uw[ui].unit = ui;
     uw[ui].tile_key_end.resize(ntile);
     for (int32_t t = 0; t < ntile; ++t) {
@@ -431,6 +469,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   P->api_splits.assign(ng + nb, 0);
   P->unit_slot = api_slot;
   std::vector<std::vector<int32_t>> bounds(nu);
+  std::vector<int32_t> shards_live;   // per tile: live shards (TileInfo::live counts partials)
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
     const int32_t tile_keys = (u.bm != kNarrowRows) ? kWideKeys : kNarrowKeys;
@@ -443,8 +482,41 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       TileInfo ti{};
       while (ti.live < u.n_splits && bounds[ui][ti.live] < uw[ui].tile_key_end[t]) ++ti.live;
       ti.part_off = -1;
+      shards_live.push_back(ti.live);
       P->tiles.push_back(ti);
     }
+  }
+  // Chains: when the MFMA-bound items of the forward form at least two
+  // (unit, KV head, M-tile) jobs per resident workgroup, the live shards of
+  // each such job run back to back in one workgroup (bin_items keeps them
+  // together, in shard order). The kernel carries the rows' (m, l, O) state
+  // from one shard into the next in registers -- the log-sum-exp merge of
+  // ADR-0060 GQA fused attention, §4, applied before anything is spilled --
+  // and writes one partial per job (or the result itself), so such a tile
+  // counts a single partial. With fewer jobs the shards stay independent
+  // items, which is what fills the device.
+  std::vector<char> chained(nu, 0);
+  {
+    int64_t jobs = 0;
+    bool multi = false;
+    for (int32_t ui = 0; ui < nu; ++ui) {
+      const UnitDesc& u = P->units[ui];
+      if (u.bm == kNarrowRows) continue;
+      for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
+        const int32_t live = shards_live[u.tile_off + t];
+        jobs += live > 0 ? in.H_kv : 0;
+        multi |= live > 1;
+      }
+    }
+    if (multi && jobs >= 2 * wide_slots)
+      for (int32_t ui = 0; ui < nu; ++ui)
+        if (P->units[ui].bm != kNarrowRows && P->units[ui].n_splits > 1) {
+          chained[ui] = 1;
+          for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
+            TileInfo& ti = P->tiles[P->units[ui].tile_off + t];
+            ti.live = std::min(ti.live, 1);
+          }
+        }
   }
   // A tile's rows need workspace rows only if some token of the tile has two
   // or more live partials over its prefix and suffix units; otherwise every
@@ -476,10 +548,11 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
       const int32_t kend = uw[ui].tile_key_end[t];
       TileInfo& ti = P->tiles[u.tile_off + t];
-      const int32_t live = ti.live;
+      const int32_t live = shards_live[u.tile_off + t];   // items of the tile per KV head
+      const int32_t parts = ti.live;                      // partials of the tile per KV head
       if (tile_needs[u.tile_off + t]) {
         ti.part_off = part;
-        part += (int64_t)in.H_kv * live * u.bm;
+        part += (int64_t)in.H_kv * parts * u.bm;
       }
       const int32_t row_begin = (int32_t)(t * u.tpt * G);
       const int32_t n_rows = (int32_t)std::min<int64_t>(u.tpt, u.n_tok - (int64_t)t * u.tpt) * G;
@@ -500,8 +573,9 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           w.key_pos0 = u.key_pos0;
           // Rows of a tile without workspace rows all write directly; the
           // kernel never uses part_row for them.
-          w.part_row = ti.part_off >= 0 ? ti.part_off + ((int64_t)kv * live + s) * u.bm : 0;
-          w.pad0 = w.pad1 = 0;
+          w.part_row = ti.part_off >= 0 ? ti.part_off + ((int64_t)kv * parts + (chained[ui] ? 0 : s)) * u.bm : 0;
+          w.chain = chained[ui] ? ((s > 0 ? kChainContinues : 0) | (s + 1 < live ? kChainContinued : 0)) : 0;
+          w.pad1 = 0;
           P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
           (u.bm != kNarrowRows ? P->wide : P->narrow).push_back(w);
         }
@@ -510,17 +584,6 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   }
   P->part_rows = part;
 
-  // Largest items first, so the tail of the grid holds the short ones.
-  auto by_cost = [](const WorkItem& a, const WorkItem& b) {
-    const int32_t ka = a.key_end - a.key_begin, kb = b.key_end - b.key_begin;
-    if (ka != kb) return ka > kb;
-    if (a.unit != b.unit) return a.unit < b.unit;
-    if (a.split != b.split) return a.split < b.split;
-    if (a.kv != b.kv) return a.kv < b.kv;
-    return a.tile < b.tile;
-  };
-  std::stable_sort(P->wide.begin(), P->wide.end(), by_cost);
-  std::stable_sort(P->narrow.begin(), P->narrow.end(), by_cost);
   bin_items(&P->wide, in.wide_per_cu * P->wide_cus, P->wide_cus, &P->wide_bins);
   bin_items(&P->narrow, in.narrow_per_cu * P->narrow_cus, P->narrow_cus, &P->narrow_bins);
 

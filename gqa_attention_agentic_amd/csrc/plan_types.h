@@ -42,7 +42,8 @@ struct UnitDesc {
   int32_t key_len;     // keys in the unit
   int32_t key_pos0;    // context position of the unit's key 0
   int32_t bm;          // row stride of an M-tile (kWideRows[Bf16] or kNarrowRows)
-  int32_t tpt;         // query tokens per M-tile: bm / G (an M-tile holds whole tokens)
+  int32_t tpt;         // query tokens per M-tile (at most bm / G: an M-tile holds whole tokens;
+                       // the unit's tokens are spread evenly over its tiles)
   int32_t tile_off;    // index of the unit's first M-tile in the tile table
   int32_t branch_lo;   // branches whose tokens form the unit: [branch_lo, branch_hi)
   int32_t branch_hi;
@@ -62,8 +63,8 @@ struct BranchDesc {
 // for the tile (shards are in key order and liveness under causality is a
 // prefix), and where the tile's partials start in the workspace.
 struct TileInfo {
-  int32_t live;        // live shards
-  int64_t part_off;    // first partial row; row layout: ((kv * live + s) * bm + r_in_tile)
+  int32_t live;        // partials per row from this tile: its live shards, or 1 when they form chains
+  int64_t part_off;    // first partial row (-1: none); row layout ((kv * live + s) * bm + r_in_tile)
 };
 
 struct WorkItem {
@@ -82,8 +83,15 @@ struct WorkItem {
   int32_t tok_begin;
   int32_t key_pos0;
   int64_t part_row;    // workspace row of the item's row 0 (its row r: part_row + r)
-  int32_t pad0, pad1;
+  int32_t chain;       // kChainContinues | kChainContinued, or 0 for an item on its own
+  int32_t pad1;
 };
+
+// WorkItem::chain bits. The shards of one (unit, KV head, M-tile) may form a
+// chain: the items run back to back in one workgroup, in shard order, and
+// the rows' (m, l, O) state passes from one to the next in registers.
+constexpr int32_t kChainContinues = 1;   // starts from the previous item's state (no Q load)
+constexpr int32_t kChainContinued = 2;   // hands its state to the next item (no write)
 
 // Per query token.
 struct TokRec {

@@ -288,10 +288,15 @@ gqa_status gqa_attn_append_times(gqa_attn* h, double* ms, int64_t* n_calls);
 /* Host-only planner check (no device use): plans the given metadata with
  * the handle-free parameters `p` for a 256-CU device with one resident
  * workgroup per CU and writes, for every work item, the tuple
- * (unit, kv_head, row_begin, n_rows, key_begin, key_end, split, kernel, bin)
- * into `items` (host, int32, 9 per item) when `items` is not NULL and `cap`
+ * (unit, kv_head, row_begin, n_rows, key_begin, key_end, split, kernel, bin,
+ *  chain)
+ * into `items` (host, int32, 10 per item) when `items` is not NULL and `cap`
  * allows. Items are listed per kernel in launch order: workgroup `bin` of
  * that kernel runs its items one after another, in the order listed.
+ * `chain` is 0 for an item on its own; otherwise bit 0 says the item starts
+ * from the previous item's (m, l, O) state and bit 1 that it hands its state
+ * to the next item instead of writing it (the shards of one M-tile and KV
+ * head run back to back, merged in registers).
  * Returns the item count through *n_items and the per-unit split counts
  * through `splits` (host, n_groups + n_branches entries, may be NULL). */
 gqa_status gqa_attn_plan_host(const gqa_attn_params* p,

@@ -66,6 +66,11 @@ PlanInput make(int H_q, int H_kv, int D, int ps, int dtype, int causal, std::vec
   return in;
 }
 
+PlanInput on_cus(int n_cu, PlanInput in) {
+  in.n_cu = n_cu;
+  return in;
+}
+
 // Checks one plan against the metadata it was built from.
 void check_plan(const std::string& name, const PlanInput& in, const Plan& P) {
   const int G = in.H_q / in.H_kv;
@@ -94,6 +99,21 @@ void check_plan(const std::string& name, const PlanInput& in, const Plan& P) {
     const std::vector<int32_t>& bins = pass ? P.narrow_bins : P.wide_bins;
     expect(!bins.empty() && bins.front() == 0 && bins.back() == (int32_t)list.size(), name + ": bins cover the items");
     for (size_t b = 0; b + 1 < bins.size(); ++b) expect(bins[b] <= bins[b + 1], name + ": bins in order");
+    // chains: inside one bin, consecutive shards of one (unit, KV head, M-tile)
+    for (size_t b = 0; b + 1 < bins.size(); ++b)
+      for (int32_t x = bins[b]; x < bins[b + 1]; ++x) {
+        const WorkItem& w = list[x];
+        expect(pass == 0 || w.chain == 0, name + ": no chains on the 32-row kernel");
+        const bool prev = x > bins[b] && (list[x - 1].chain & kChainContinued);
+        expect(prev == ((w.chain & kChainContinues) != 0), name + ": a chain's items are consecutive");
+        if (prev) {
+          const WorkItem& p = list[x - 1];
+          expect(p.unit == w.unit && p.kv == w.kv && p.tile == w.tile && p.split + 1 == w.split &&
+                     p.key_end == w.key_begin && p.part_row == w.part_row,
+                 name + ": a chain continues its own M-tile's next shard");
+        }
+        if (x + 1 == bins[b + 1]) expect(!(w.chain & kChainContinued), name + ": a chain ends inside its bin");
+      }
     for (const WorkItem& w : list) {
       ++n_items;
       expect(w.unit >= 0 && w.unit < (int)P.units.size(), name + ": item unit");
@@ -122,7 +142,9 @@ void check_plan(const std::string& name, const PlanInput& in, const Plan& P) {
           ++cover[std::make_tuple(w.unit, tok, g, w.kv, k)];
         }
       }
-      for (int tok : toks) ++items_per_tok_kv[{tok, w.kv}];
+      // a chain of shards leaves one partial: count its first item only
+      if (!(w.chain & kChainContinues))
+        for (int tok : toks) ++items_per_tok_kv[{tok, w.kv}];
     }
   }
   // expected visible pairs, unit by unit
@@ -176,6 +198,11 @@ void run_case(const Case& c) {
   const std::string err = build_plan(c.in, &P);
   expect(err.empty(), c.name + ": planned (" + err + ")");
   if (err.empty()) check_plan(c.name, c.in, P);
+  if (err.empty() && c.name.find("chains") != std::string::npos) {
+    bool any = false;
+    for (const WorkItem& w : P.wide) any |= w.chain != 0;
+    expect(any, c.name + ": the shards of its M-tiles form chains");
+  }
 }
 
 }  // namespace
@@ -198,6 +225,10 @@ int main() {
                                                            {0, 1, 5}, {0, 1, 6}, {0, 1, 7}, {0, 1, 8}})},
       {"huge_splits", make(16, 2, 128, 16, 0, 1, {40}, {{0, 3, 3}}, {4096, 4096})},
       {"decode_8k", make(64, 8, 128, 16, 0, 0, {8192}, {{0, 1, 0}}, {32, 0})},
+      // many (KV head, M-tile) jobs per workgroup on an 8-CU device: chains
+      {"prefill_chains", on_cus(8, make(16, 4, 128, 16, 0, 1, {300}, {{0, 300, 0}}, {3, 0}))},
+      {"prefill_chains_fp32", on_cus(8, make(16, 4, 64, 16, 1, 1, {200}, {{0, 200, 0}}, {4, 0}))},
+      {"join_chains", on_cus(8, make(16, 4, 128, 16, 0, 1, {150}, {{0, 250, 250}}, {3, 2}))},
   };
   for (const Case& c : cases) run_case(c);
 

@@ -72,7 +72,7 @@ def _covered_pairs(w, items):
         first_tok.setdefault(b.group, qb[bi])
         first_tok[ng + bi] = qb[bi]
     got = []
-    for (slot, kv, r0, nr, k0, k1, split, kern, _bin) in items:
+    for (slot, kv, r0, nr, k0, k1, split, kern, _bin, _chain) in items:
         for r in range(r0, r0 + nr):
             tok = first_tok[slot] + r // G_
             g = r % G_
@@ -115,7 +115,7 @@ def test_items_partition_visible_pairs(w):
     assert stats["n_items_wide"] + stats["n_items_narrow"] == len(items)
     # A unit on the 32-row kernel fits one M-tile, so a narrow item's tokens
     # hold at most 32 rows (the size of that kernel's combination table).
-    for (_slot, _kv, r0, nr, _k0, _k1, _split, kern, _bin) in items:
+    for (_slot, _kv, r0, nr, _k0, _k1, _split, kern, _bin, _chain) in items:
         if kern == 1:
             assert r0 == 0 and nr <= 32
 
@@ -191,12 +191,29 @@ def _item_cost(it):
     return it[5] - it[4] + 96       # keys plus the planner's fixed per-item cost
 
 
+def _jobs(its):
+    """Consecutive items of one workgroup grouped into jobs: an item on its
+    own, or a chain (first item hands its state on, the rest continue)."""
+    jobs = []
+    for it in its:
+        if jobs and it[9] & 1:
+            jobs[-1].append(it)
+        else:
+            jobs.append([it])
+    return jobs
+
+
+def _job_cost(job):
+    return sum(it[5] - it[4] for it in job) + 96 + 16 * (len(job) - 1)
+
+
 @pytest.mark.parametrize("name", ["fanout_8x20_32k", "decode_8k", "prefill_32k", "mixed_32dec_64x4"])
 def test_bins_pack_items_onto_resident_workgroups(name):
     """Each kernel's items are dealt to at most 256 workgroups (one per CU);
-    a workgroup's items are contiguous and largest first; no workgroup's
-    load exceeds the list-scheduling bound (mean load + largest item) by
-    more than the 2% that the XCD placement may cost."""
+    a workgroup's items are contiguous and its jobs (items, or chains of
+    one M-tile's shards) largest first; no workgroup's load exceeds the
+    list-scheduling bound (mean load + largest job) by more than the 2% that
+    the XCD placement may cost."""
     items, _, _ = _plan(get_workload(name))
     for kern in (0, 1):
         its = [it for it in items if it[7] == kern]
@@ -207,12 +224,14 @@ def test_bins_pack_items_onto_resident_workgroups(name):
         n_bins = max(bins) + 1
         assert n_bins <= 256 and n_bins <= len(its)
         load = [0] * n_bins
-        for it in its:
-            load[it[8]] += _item_cost(it)
-        for a, b in zip(its, its[1:]):
-            if a[8] == b[8]:
-                assert _item_cost(a) >= _item_cost(b)
-        bound = sum(load) / n_bins + max(_item_cost(it) for it in its)
+        jobs = []
+        for b in range(n_bins):
+            jobs_b = _jobs([it for it in its if it[8] == b])
+            costs = [_job_cost(j) for j in jobs_b]
+            assert costs == sorted(costs, reverse=True), "jobs of a workgroup are not largest first"
+            load[b] = sum(costs)
+            jobs += jobs_b
+        bound = sum(load) / n_bins + max(_job_cost(j) for j in jobs)
         assert max(load) <= 1.02 * bound, (max(load), bound)
 
 
@@ -233,15 +252,47 @@ def test_fanout_bins_balance_and_share_l2():
     assert all(len(v) == 1 for v in xcd.values())
 
 
-@pytest.mark.parametrize("name,launch", [("decode_8k", 0), ("fanout_8x20_32k", 1), ("prefill_32k", 1),
-                                         ("mixed_32dec_64x4", 1)])
-def test_merge_launch_only_when_wide_partials(name, launch):
+@pytest.mark.parametrize("name,rows,launch", [("decode_8k", True, 0), ("fanout_8x20_32k", True, 1),
+                                              ("prefill_32k", False, 0), ("mixed_32dec_64x4", True, 1)])
+def test_merge_launch_only_when_wide_partials(name, rows, launch):
     """Rows whose partials all come from the narrow kernel are combined inside
     it: a decode forward has no separate merge launch; workloads with rows
-    split over the MFMA kernel keep it."""
+    split over the MFMA kernel keep it. The prefill's 8 shards per M-tile
+    form chains merged in registers: every row has one partial, written as
+    the result, and nothing is left to merge."""
     _, _, stats = _plan(get_workload(name))
-    assert stats["n_merge_rows"] > 0
+    assert (stats["n_merge_rows"] > 0) == rows
     assert stats["merge_launch"] == launch
+    if not rows:
+        assert stats["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("name,chains", [("prefill_32k", True), ("join_8000_32k", None), ("fanout_8x20_32k", False),
+                                         ("join_400_32k", False)])
+def test_shards_of_an_m_tile_chain_when_work_is_plentiful(name, chains):
+    """With at least two (unit, KV head, M-tile) jobs per workgroup the live
+    shards of each job form a chain: consecutive items of one workgroup, in
+    shard order over contiguous keys, the first handing its state on, the
+    last writing it, those between doing both. With fewer jobs (fan-out,
+    400-token join) no item chains."""
+    w = get_workload(name)
+    items, splits, _ = _plan(w)
+    wide = [it for it in items if it[7] == 0]
+    chained = [it for it in wide if it[9]]
+    if chains is False:
+        assert not chained
+        return
+    if chains and splits[0] > 1:
+        assert chained
+    for b in {it[8] for it in wide}:
+        for job in _jobs([it for it in wide if it[8] == b]):
+            if len(job) == 1:
+                assert job[0][9] == 0
+                continue
+            assert [it[6] for it in job] == list(range(len(job)))                  # shard order
+            assert len({(it[0], it[1], it[2]) for it in job}) == 1                 # one unit, head, M-tile
+            assert all(a[5] == b[4] for a, b in zip(job, job[1:]))                 # contiguous keys
+            assert job[0][9] == 2 and job[-1][9] == 1 and all(it[9] == 3 for it in job[1:-1])
 
 
 @pytest.mark.parametrize("name,split", [("decode_8k", False), ("fanout_8x20_32k", False),
@@ -304,6 +355,28 @@ def test_m_tiles_hold_whole_tokens():
     for (_slot, _kv, r0, nr, *_rest) in items:
         assert r0 % 3 == 0 and nr % 3 == 0 and nr <= 255
     assert set(_covered_pairs(w, items)) == _expected_pairs(w)
+
+
+@pytest.mark.parametrize("agents,G", [(2, 8), (4, 8), (8, 8), (8, 2), (8, 4), (3, 1)])
+def test_m_tiles_of_a_unit_are_balanced(agents, G):
+    """A unit's tokens are spread evenly over its M-tiles (the same number of
+    tokens per tile, the last short by fewer tokens than there are tiles, so
+    active waves differ by at most one), so no tile of a shared prefix is a small
+    remnant that streams the prefix's K/V at another pace than the others.
+    (Coverage of these plans is checked on smaller prefixes above and in the
+    sanitizer build.)"""
+    w = custom("bal", H_q=8 * G, H_kv=8, shared=(32768,), branches=tuple((0, 20, 512) for _ in range(agents)),
+               seed=3)
+    items, _, _ = _plan(w)
+    rows = {}
+    for (slot, kv, r0, nr, *_rest) in items:
+        rows.setdefault((slot, kv), set()).add((r0, nr))
+    for key, tiles in rows.items():
+        counts = [nr for _, nr in tiles]
+        waves = [-(-nr // 32) for nr in counts]        # active 32-row waves of each tile
+        assert max(waves) - min(waves) <= 1, (key, sorted(tiles))
+        assert max(counts) - min(counts) <= (len(counts) - 1) * G, (key, sorted(tiles))
+        assert sum(counts) == (agents * 20 if key[0] == 0 else 20) * G, key
 
 
 @pytest.mark.parametrize("meta,msg", [

@@ -284,6 +284,26 @@ def test_unused_slots_of_last_pages_never_read(name):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("dtype,d,n,splits", [("bf16", 128, 4096, 4), ("fp32", 64, 2048, 3)])
+def test_chained_shards_prefill(dtype, d, n, splits):
+    """A causal prefill with H_q 64, H_kv 8 and pinned shards, long enough
+    that its (KV head, M-tile) jobs outnumber the workgroups twice over: the
+    shards of each M-tile run as a chain, merged in registers, and every row
+    is written directly (no partials, no merge launch). Compared with the
+    oracle on every 8th token plus the M-tile, KV-tile and shard edges."""
+    w = custom(f"chain_prefill_{dtype}", dtype=dtype, H_q=64, H_kv=8, d=d, shared=(n,), branches=((0, n, 0),),
+               seed=131, splits=[splits, 0])
+    inp = generate(w, "cuda")
+    o, lse, h = H.run_library(w, inp)
+    st = h.plan_stats()
+    H.say(f"  {w.name}: plan {st}")
+    assert st["merge_launch"] == 0 and st["n_merge_rows"] == 0 and st["workspace_bytes"] == 0
+    m_tile = (256 if dtype == "bf16" else 128) // 8
+    toks = sorted(set(range(0, n, 8)) | _edges(n, -(-n // splits), m_tile))
+    ref = H.oracle_rows(w, inp, tokens=toks)
+    H.compare(w, o, lse, ref[0], ref[1], ref[2], label=f"{w.name} ({len(toks)}/{n} tokens)")
+
+
 # ------------------------------------------------ full-size configurations --
 def _parity(name, tokens=None):
     """The library's output at a full-size workload against the oracle on
