@@ -328,6 +328,10 @@ gqa_status launch_forward(gqa_attn* h, const ForwardArgs& f, const gqa::Plan& Q,
   a.causal = f.causal;
   a.n_q_tokens = Q.n_q_tokens;
   a.scale_log2 = h->p.softmax_scale * 1.4426950408889634f;
+  // Device-scope partial stores without a release fence when every
+  // workgroup of the bf16 narrow kernel runs a single item (see
+  // combine_if_last in attention.hip).
+  a.coherent_parts = (h->p.dtype == GQA_BF16 && !Q.narrow.empty() && Q.narrow.size() + 1 == Q.narrow_bins.size()) ? 1 : 0;
 
   auto ev = [&](int k) -> hipEvent_t { return tm ? tm->ev[k] : nullptr; };
   if (tm) {

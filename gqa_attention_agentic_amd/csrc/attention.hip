@@ -447,8 +447,19 @@ __device__ __forceinline__ RowDest row_dest(const AttnArgs& a, const WorkItem& i
   return d;
 }
 
+// An 8-byte store at device scope: on gfx950 it is written through to the
+// device's coherence point, so once the issuing thread's stores have
+// completed (vmcnt 0) any CU of any XCD that acquires at device scope reads
+// it -- no L2 write-back fence is needed for it.
+__device__ __forceinline__ void store_device(void* p, float x, float y) {
+  const uint64_t v = ((uint64_t)__float_as_uint(y) << 32) | __float_as_uint(x);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Final or partial write of one lane's row for O^T blocks [db0, db1).
-template <class C, typename T, int D>
+// COHERENT: the partial is written with device-scope stores (see
+// combine_if_last).
+template <class C, typename T, int D, bool COHERENT = false>
 __device__ __forceinline__ void write_row_to(const AttnArgs& a, const RowDest& dst, bool ok, float m, float l,
                                              const f32x16_t* o, int db0, int db1, bool write_scalars, int h) {
   if (!ok) return;
@@ -478,11 +489,19 @@ __device__ __forceinline__ void write_row_to(const AttnArgs& a, const RowDest& d
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * db + 8 * q4 + 4 * h;
-        *(float4*)(po + d0) = make_float4(o[db - db0][4 * q4 + 0], o[db - db0][4 * q4 + 1],
-                                          o[db - db0][4 * q4 + 2], o[db - db0][4 * q4 + 3]);
+        if (COHERENT) {
+          store_device(po + d0, o[db - db0][4 * q4 + 0], o[db - db0][4 * q4 + 1]);
+          store_device(po + d0 + 2, o[db - db0][4 * q4 + 2], o[db - db0][4 * q4 + 3]);
+        } else {
+          *(float4*)(po + d0) = make_float4(o[db - db0][4 * q4 + 0], o[db - db0][4 * q4 + 1],
+                                            o[db - db0][4 * q4 + 2], o[db - db0][4 * q4 + 3]);
+        }
       }
     }
-    if (write_scalars && h == 0) a.part_ml[dst.row] = make_float2(m, l);
+    if (write_scalars && h == 0) {
+      if (COHERENT) store_device(&a.part_ml[dst.row], m, l);
+      else a.part_ml[dst.row] = make_float2(m, l);
+    }
   }
 }
 
@@ -596,12 +615,22 @@ __device__ __forceinline__ T plan_load(const T* p) {
 //    has at most BM rows and tokens).
 //  * After its rows are written, each such token's counter (one per KV
 //    head) is incremented; the item that brings it to the planned number of
-//    arrivals combines the token's rows. Release before the increment and
-//    acquire after the winning one (device scope: the XCDs' L2 caches are
-//    not coherent with each other) make every other item's partials
-//    visible. The winner resets the counter after its combination, so all
-//    counters are zero again when the launch ends. Work per workgroup is
-//    bounded and no thread waits on another workgroup.
+//    arrivals combines the token's rows. The XCDs' L2 caches are not
+//    coherent with each other, so every other item's partials must reach
+//    device scope before its increment, and the winner acquires at device
+//    scope after its own. Two ways:
+//      - partials in ordinary stores, then a device-scope release fence
+//        (write-back of the L2's dirty lines) before the increment;
+//      - partials in device-scope stores (a.coherent_parts), which need
+//        only to have completed before the increment. Used when every
+//        workgroup runs a single item: all of them then finish at once,
+//        and hundreds of simultaneous L2 write-backs queue up (measured on
+//        MI355X: ~4.6 us from stores done to arrival at the 8k decode's 256
+//        items); with several items per workgroup the arrivals are spread
+//        out and ordinary stores plus the fence are cheaper.
+//    The winner resets the counter after its combination, so all counters
+//    are zero again when the launch ends. Work per workgroup is bounded and
+//    no thread waits on another workgroup.
 //  * Two threads share each (row, 4 d values): each folds one half of the
 //    row's partials, so a decode row's shards arrive in one round of loads,
 //    and the halves are joined through a lane exchange.
@@ -662,7 +691,7 @@ __device__ __forceinline__ void combine_if_last(const AttnArgs& a, int tid, Comb
     int w = 0;
     if (need > 0) {
       int* c = a.counters + (int64_t)(tok0 + k) * a.H_kv + kv;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (!a.coherent_parts) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       if (atomicAdd(c, 1) == need - 1) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         w = 1;
@@ -1313,7 +1342,10 @@ attn_narrow_dma(AttnArgs a) {
         for (int k = 0; k < C::WAVES; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
         acc[r] = x;
       }
-      write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
+      if (a.coherent_parts)
+        write_row_to<C, uint16_t, D, true>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
+      else
+        write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
     }
     combine_if_last<uint16_t, D, C::THREADS>(a, tid, &cl);
   }

@@ -33,7 +33,10 @@ struct AttnArgs {
   int32_t causal;
   int32_t n_q_tokens;
   float scale_log2;     // softmax_scale * log2(e)
-  int32_t pad;
+  // Narrow kernel, each workgroup runs one item: partials are written with
+  // device-scope stores and the arrival needs no release fence (see
+  // combine_if_last); otherwise ordinary stores and a release fence.
+  int32_t coherent_parts;
 };
 
 // Attention over a work-item list: one workgroup per bin (a.bins holds

@@ -85,6 +85,13 @@ SMALL = {
     "batched_paged_decodes": lambda: custom("batched_paged_decodes", shared=(0,),
                                             branches=((0, 1, 3000), (0, 1, 1200), (0, 1, 5000), (0, 1, 17)),
                                             seed=125),
+    # 48 paged decodes forced to 4 shards each: 384 narrow items on at most
+    # 256 workgroups, so workgroups run several items and the narrow kernel
+    # takes its path for staggered arrivals (ordinary partial stores and a
+    # release fence); the decodes above run one item per workgroup.
+    "decodes_several_items_per_workgroup": lambda: custom(
+        "decodes_several_items_per_workgroup", shared=(0,), branches=tuple((0, 1, 1500 + 37 * k) for k in range(48)),
+        seed=127, splits=[0] + [4] * 48),
     # Non-causal multi-token queries: every key of the context is visible.
     "noncausal_fanout": lambda: custom("noncausal_fanout", shared=(300,), branches=((0, 5, 40), (0, 7, 21)),
                                        causal=False, seed=126),
