@@ -44,8 +44,38 @@ std::vector<int32_t> shard_bounds(int32_t L, int32_t S, int32_t tile) {
 
 struct UnitWork {
   int32_t unit;
+  std::vector<int32_t> tile_tok;       // unit-local first token of each M-tile, then n_tok
   std::vector<int32_t> tile_key_end;   // causal clamp per M-tile (unit-local keys)
+  int32_t tile_of(int32_t tok) const {  // M-tile of unit-local token tok
+    return (int32_t)(std::upper_bound(tile_tok.begin(), tile_tok.end(), tok) - tile_tok.begin()) - 1;
+  }
 };
+
+// Token boundaries of the M-tiles of a unit with n_tok tokens of G rows each,
+// at most `cap` tokens per tile (bm / G: a tile holds whole tokens). The
+// fewest tiles are used and the work is spread evenly over them, so that the
+// tiles of one unit keep the same pace through its K/V tiles (a full tile
+// next to a small remnant would run behind it and fetch the shared K/V a
+// second time). A wave computes 32 rows whether or not they are all valid,
+// so when whole tokens fill whole waves (G divides 32) the tiles get whole
+// waves each -- as many waves as the tokens need, the counts differing by at
+// most one; otherwise the tokens themselves are spread evenly.
+std::vector<int32_t> tile_bounds(int32_t n_tok, int32_t G, int32_t cap) {
+  const int32_t ntile = (int32_t)ceil_div(n_tok, cap);
+  std::vector<int32_t> b(1, 0);
+  if (32 % G == 0 && cap % (32 / G) == 0) {
+    const int32_t tpw = 32 / G;                       // tokens per wave
+    const int32_t waves = (int32_t)ceil_div(n_tok, tpw);
+    const int32_t per = waves / ntile, extra = waves % ntile;
+    for (int32_t t = 0; t < ntile; ++t)
+      b.push_back(std::min(n_tok, b.back() + (per + (t < extra ? 1 : 0)) * tpw));
+  } else {
+    const int32_t tpt = (int32_t)ceil_div(n_tok, ntile);
+    for (int32_t t = 0; t < ntile; ++t) b.push_back(std::min(n_tok, b.back() + tpt));
+  }
+  b.back() = n_tok;
+  return b;
+}
 
 // Makespan of a list of item costs on `slots` identical workers, largest
 // first (list scheduling in the order the kernel's grid is issued).
@@ -338,11 +368,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   }
 
   // M-tiles (whole tokens, so every row of a token shares one M-tile of
-  // each unit) and their causal key clamp. A unit's tokens are spread evenly
-  // over the fewest tiles of at most bm / G tokens: tiles of one unit then
-  // have the same number of active waves and stream the unit's K/V tiles at
-  // the same pace, so one L2 serves all of them (a full tile next to a
-  // remnant would run behind it and fetch the shared prefix a second time).
+  // each unit; see tile_bounds) and their causal key clamp.
   const int32_t nu = (int32_t)P->units.size();
   std::vector<UnitWork> uw(nu);
   for (int32_t ui = 0; ui < nu; ++ui) {
@@ -350,12 +376,13 @@ std::string build_plan(const PlanInput& in, Plan* P) {
     const int64_t M = (int64_t)u.n_tok * G;
     u.bm = (M <= kNarrowRows) ? kNarrowRows : wide_rows;
     const int32_t cap = u.bm / G;
-    const int32_t ntile = (int32_t)ceil_div(u.n_tok, cap);
-    u.tpt = (int32_t)ceil_div(u.n_tok, ntile);
     uw[ui].unit = ui;
+    uw[ui].tile_tok = tile_bounds(u.n_tok, G, cap);
+    const int32_t ntile = (int32_t)uw[ui].tile_tok.size() - 1;
+    u.tpt = uw[ui].tile_tok[1] - uw[ui].tile_tok[0];
     uw[ui].tile_key_end.resize(ntile);
     for (int32_t t = 0; t < ntile; ++t) {
-      const int64_t t0 = (int64_t)t * u.tpt, t1 = std::min<int64_t>(u.n_tok, t0 + u.tpt);
+      const int64_t t0 = uw[ui].tile_tok[t], t1 = uw[ui].tile_tok[t + 1];
       int32_t pmax = -1;
       for (int64_t tok = u.tok_begin + t0; tok < u.tok_begin + t1; ++tok)
         pmax = std::max(pmax, pos_of_tok[tok]);
@@ -442,7 +469,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           std::vector<int32_t> bnd = shard_bounds(u.key_len, s, kWideKeys);
           for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
             const int32_t kend = uw[ui].tile_key_end[t];
-            const int64_t rows = std::min<int64_t>(u.tpt, u.n_tok - (int64_t)t * u.tpt) * G;
+            const int64_t rows = (int64_t)(uw[ui].tile_tok[t + 1] - uw[ui].tile_tok[t]) * G;
             int live = 0;
             for (size_t k = 0; k + 1 < bnd.size(); ++k) {
               if (bnd[k] >= kend) break;
@@ -531,7 +558,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       for (int x = 0; x < 2; ++x) {
         if (us[x] < 0) continue;
         const UnitDesc& u = P->units[us[x]];
-        tix[x] = u.tile_off + (tok - u.tok_begin) / u.tpt;
+        tix[x] = u.tile_off + uw[us[x]].tile_of(tok - u.tok_begin);
         n += P->tiles[tix[x]].live;
       }
       if (n >= 2)
@@ -554,8 +581,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
         ti.part_off = part;
         part += (int64_t)in.H_kv * parts * u.bm;
       }
-      const int32_t row_begin = (int32_t)(t * u.tpt * G);
-      const int32_t n_rows = (int32_t)std::min<int64_t>(u.tpt, u.n_tok - (int64_t)t * u.tpt) * G;
+      const int32_t row_begin = uw[ui].tile_tok[t] * G;
+      const int32_t n_rows = (uw[ui].tile_tok[t + 1] - uw[ui].tile_tok[t]) * G;
       for (int32_t s = 0; s < live; ++s) {
         for (int32_t kv = 0; kv < in.H_kv; ++kv) {
           WorkItem w{};
@@ -608,9 +635,9 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       for (int x = 0; x < 2; ++x) {
         if (us[x] < 0) continue;
         const UnitDesc& u = P->units[us[x]];
-        const int32_t tl = (tok - u.tok_begin) / u.tpt;
+        const int32_t tl = uw[us[x]].tile_of(tok - u.tok_begin);
         const TileInfo& ti = P->tiles[u.tile_off + tl];
-        c.p[x] = ti.part_off + (int64_t)(tok - u.tok_begin - tl * u.tpt) * G;
+        c.p[x] = ti.part_off + (int64_t)(tok - u.tok_begin - uw[us[x]].tile_tok[tl]) * G;
         c.live[x] = ti.live;
         c.bm[x] = u.bm;
         n += ti.live;

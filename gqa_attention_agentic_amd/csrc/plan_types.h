@@ -42,8 +42,8 @@ struct UnitDesc {
   int32_t key_len;     // keys in the unit
   int32_t key_pos0;    // context position of the unit's key 0
   int32_t bm;          // row stride of an M-tile (kWideRows[Bf16] or kNarrowRows)
-  int32_t tpt;         // query tokens per M-tile (at most bm / G: an M-tile holds whole tokens;
-                       // the unit's tokens are spread evenly over its tiles)
+  int32_t tpt;         // query tokens of the unit's first M-tile (at most bm / G: an M-tile holds
+                       // whole tokens; the planner spreads the unit's tokens evenly over its tiles)
   int32_t tile_off;    // index of the unit's first M-tile in the tile table
   int32_t branch_lo;   // branches whose tokens form the unit: [branch_lo, branch_hi)
   int32_t branch_hi;
