@@ -126,8 +126,9 @@ double lpt_assign(const std::vector<double>& cost, const std::vector<size_t>& or
 // workgroup, so that every workgroup starts at once and runs its bin's items
 // back to back; the hardware then never has to queue a workgroup behind a
 // long one. The unit of packing is a job: one item, or a chain (the
-// consecutive shards of one (unit, KV head, M-tile), which must run in
-// shard order in one workgroup). Jobs are placed largest first, so the tail
+// consecutive shards of one (unit, KV head, M-tile) -- for a group with a
+// single branch, the prefix's shards followed by the suffix's -- which must
+// run in order in one workgroup). Jobs are placed largest first, so the tail
 // of each bin holds the short ones.
 //
 // Workgroups are dealt to the 8 XCDs of the chip round-robin by launch
@@ -138,27 +139,25 @@ double lpt_assign(const std::vector<double>& cost, const std::vector<size_t>& or
 // first, and each XCD's jobs to its least-loaded bins. That placement is
 // kept unless plain list scheduling over all bins would finish more than 2%
 // sooner.
-void bin_items(std::vector<WorkItem>* items, int slots, int n_cu, std::vector<int32_t>* bins) {
+void bin_items(std::vector<WorkItem>* items, const std::vector<int64_t>& chain_key, int slots, int n_cu,
+               std::vector<int32_t>* bins) {
   const size_t n = items->size();
   bins->assign(1, 0);
   if (n == 0) return;
-  // Jobs: chains keyed by (unit, KV head, M-tile), every other item alone;
-  // a job's items in shard order.
+  // Jobs: the items of one chain (same chain_key, >= 0), in the order they
+  // were made, which is chain order; every other item alone.
   std::vector<std::vector<size_t>> job;
   {
-    std::map<std::array<int32_t, 3>, size_t> chain_job;
+    std::map<int64_t, size_t> chain_job;
     for (size_t i = 0; i < n; ++i) {
-      const WorkItem& w = (*items)[i];
-      if (w.chain == 0) {
+      if ((*items)[i].chain == 0) {
         job.push_back({i});
         continue;
       }
-      auto ins = chain_job.emplace(std::array<int32_t, 3>{w.unit, w.kv, w.tile}, job.size());
+      auto ins = chain_job.emplace(chain_key[i], job.size());
       if (ins.second) job.emplace_back();
       job[ins.first->second].push_back(i);
     }
-    for (auto& j : job)
-      std::sort(j.begin(), j.end(), [&](size_t a, size_t b) { return (*items)[a].split < (*items)[b].split; });
   }
   const size_t nj = job.size();
   const int nb = (int)std::min<int64_t>((int64_t)nj, std::max(1, slots));
@@ -525,19 +524,17 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   std::vector<char> chained(nu, 0);
   {
     int64_t jobs = 0;
-    bool multi = false;
     for (int32_t ui = 0; ui < nu; ++ui) {
       const UnitDesc& u = P->units[ui];
       if (u.bm == kNarrowRows) continue;
       for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
         const int32_t live = shards_live[u.tile_off + t];
         jobs += live > 0 ? in.H_kv : 0;
-        multi |= live > 1;
       }
     }
-    if (multi && jobs >= 2 * wide_slots)
+    if (jobs >= 2 * wide_slots)
       for (int32_t ui = 0; ui < nu; ++ui)
-        if (P->units[ui].bm != kNarrowRows && P->units[ui].n_splits > 1) {
+        if (P->units[ui].bm != kNarrowRows) {
           chained[ui] = 1;
           for (size_t t = 0; t < uw[ui].tile_key_end.size(); ++t) {
             TileInfo& ti = P->tiles[P->units[ui].tile_off + t];
@@ -545,6 +542,35 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           }
         }
   }
+  // Across units: when a group has a single branch, its prefix unit and its
+  // suffix unit have the same tokens cut into the same M-tiles, so each
+  // (KV head, M-tile) chain can run on from the prefix's last shard into the
+  // suffix's shards and end with the row's only partial -- the result,
+  // written directly (a continuation prefill after a join). The prefix
+  // tiles then leave no partial of their own.
+  std::vector<char> cross(nb, 0);
+  for (int32_t b = 0; b < nb; ++b) {
+    const BranchDesc& br = P->branches[b];
+    if (br.unit_sh < 0 || br.unit_pr < 0 || !chained[br.unit_sh] || !chained[br.unit_pr]) continue;
+    const UnitDesc& us = P->units[br.unit_sh];
+    const UnitDesc& up = P->units[br.unit_pr];
+    if (us.branch_hi - us.branch_lo != 1 || us.tok_begin != up.tok_begin || uw[br.unit_sh].tile_tok != uw[br.unit_pr].tile_tok)
+      continue;
+    bool ok = true;
+    for (size_t t = 0; t + 1 < uw[br.unit_pr].tile_tok.size(); ++t)
+      ok &= shards_live[up.tile_off + t] > 0 && shards_live[us.tile_off + t] > 0;
+    if (!ok) continue;
+    cross[b] = 1;
+    for (size_t t = 0; t + 1 < uw[br.unit_sh].tile_tok.size(); ++t) P->tiles[us.tile_off + t].live = 0;
+  }
+  std::vector<int32_t> cross_into(nu, -1);   // prefix unit -> the suffix unit its chains run into
+  std::vector<char> cross_from(nu, 0);       // suffix unit whose chains start in the prefix
+  for (int32_t b = 0; b < nb; ++b)
+    if (cross[b]) {
+      cross_into[P->branches[b].unit_sh] = P->branches[b].unit_pr;
+      cross_from[P->branches[b].unit_pr] = 1;
+    }
+
   // A tile's rows need workspace rows only if some token of the tile has two
   // or more live partials over its prefix and suffix units; otherwise every
   // row of the tile writes O / l directly.
@@ -566,8 +592,10 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           if (tix[x] >= 0) tile_needs[tix[x]] = 1;
     }
   }
-  // Workspace offsets and items.
+  // Workspace offsets and items (with the chain key of each, for binning:
+  // a chain is named by its first unit, KV head and M-tile).
   int64_t part = 0;
+  std::vector<int64_t> key_wide, key_narrow;
   for (int32_t ui = 0; ui < nu; ++ui) {
     UnitDesc& u = P->units[ui];
     const int32_t tile_keys = (u.bm != kNarrowRows) ? kWideKeys : kNarrowKeys;
@@ -601,9 +629,16 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           // Rows of a tile without workspace rows all write directly; the
           // kernel never uses part_row for them.
           w.part_row = ti.part_off >= 0 ? ti.part_off + ((int64_t)kv * parts + (chained[ui] ? 0 : s)) * u.bm : 0;
-          w.chain = chained[ui] ? ((s > 0 ? kChainContinues : 0) | (s + 1 < live ? kChainContinued : 0)) : 0;
+          const bool first = s == 0 && !cross_from[ui], last = s + 1 == live && cross_into[ui] < 0;
+          w.chain = chained[ui] ? ((first ? 0 : kChainContinues) | (last ? 0 : kChainContinued)) : 0;
           w.pad1 = 0;
           P->n_kv_tiles += ceil_div(w.key_end - w.key_begin, tile_keys);
+          int32_t head_unit = ui;   // the unit a cross-unit chain starts in
+          if (cross_from[ui])
+            for (int32_t v = 0; v < nu; ++v)
+              if (cross_into[v] == ui) head_unit = v;
+          const int64_t key = ((int64_t)head_unit * in.H_kv + kv) * (1 << 20) + (int64_t)t;
+          (u.bm != kNarrowRows ? key_wide : key_narrow).push_back(key);
           (u.bm != kNarrowRows ? P->wide : P->narrow).push_back(w);
         }
       }
@@ -611,8 +646,8 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   }
   P->part_rows = part;
 
-  bin_items(&P->wide, in.wide_per_cu * P->wide_cus, P->wide_cus, &P->wide_bins);
-  bin_items(&P->narrow, in.narrow_per_cu * P->narrow_cus, P->narrow_cus, &P->narrow_bins);
+  bin_items(&P->wide, key_wide, in.wide_per_cu * P->wide_cus, P->wide_cus, &P->wide_bins);
+  bin_items(&P->narrow, key_narrow, in.narrow_per_cu * P->narrow_cus, P->narrow_cus, &P->narrow_bins);
 
   // Per-token records. All G rows of a token lie in one M-tile of each of
   // its units, so they have the same partials: live shards of that tile in

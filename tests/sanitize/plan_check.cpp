@@ -108,9 +108,20 @@ void check_plan(const std::string& name, const PlanInput& in, const Plan& P) {
         expect(prev == ((w.chain & kChainContinues) != 0), name + ": a chain's items are consecutive");
         if (prev) {
           const WorkItem& p = list[x - 1];
-          expect(p.unit == w.unit && p.kv == w.kv && p.tile == w.tile && p.split + 1 == w.split &&
-                     p.key_end == w.key_begin && p.part_row == w.part_row,
-                 name + ": a chain continues its own M-tile's next shard");
+          if (p.unit == w.unit) {
+            expect(p.kv == w.kv && p.tile == w.tile && p.split + 1 == w.split && p.key_end == w.key_begin &&
+                       p.part_row == w.part_row,
+                   name + ": a chain continues its own M-tile's next shard");
+          } else {
+            // from a single-branch group's prefix into that branch's suffix
+            const UnitDesc& pu = P.units[p.unit];
+            const UnitDesc& wu = P.units[w.unit];
+            expect(pu.kind == kShared && wu.kind == kPrivate && pu.branch_lo == wu.branch_lo &&
+                       pu.branch_hi == pu.branch_lo + 1 && p.kv == w.kv && p.tile == w.tile &&
+                       p.split + 1 == pu.n_splits && w.split == 0 && p.row_begin == w.row_begin &&
+                       p.n_rows == w.n_rows && p.tok_begin == w.tok_begin,
+                   name + ": a chain crosses only from a lone branch's prefix into its suffix");
+          }
         }
         if (x + 1 == bins[b + 1]) expect(!(w.chain & kChainContinued), name + ": a chain ends inside its bin");
       }
@@ -229,6 +240,8 @@ int main() {
       {"prefill_chains", on_cus(8, make(16, 4, 128, 16, 0, 1, {300}, {{0, 300, 0}}, {3, 0}))},
       {"prefill_chains_fp32", on_cus(8, make(16, 4, 64, 16, 1, 1, {200}, {{0, 200, 0}}, {4, 0}))},
       {"join_chains", on_cus(8, make(16, 4, 128, 16, 0, 1, {150}, {{0, 250, 250}}, {3, 2}))},
+      {"join_chains_one_shard", on_cus(8, make(16, 4, 128, 16, 0, 1, {150}, {{0, 250, 250}}, {1, 1}))},
+      {"fanout_chains", on_cus(8, make(16, 4, 128, 16, 0, 1, {150}, {{0, 70, 40}, {0, 90, 30}}, {3, 2, 2}))},
   };
   for (const Case& c : cases) run_case(c);
 

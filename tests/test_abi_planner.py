@@ -253,7 +253,8 @@ def test_fanout_bins_balance_and_share_l2():
 
 
 @pytest.mark.parametrize("name,rows,launch", [("decode_8k", True, 0), ("fanout_8x20_32k", True, 1),
-                                              ("prefill_32k", False, 0), ("mixed_32dec_64x4", True, 1)])
+                                              ("prefill_32k", False, 0), ("mixed_32dec_64x4", True, 1),
+                                              ("join_8000_32k", False, 0)])
 def test_merge_launch_only_when_wide_partials(name, rows, launch):
     """Rows whose partials all come from the narrow kernel are combined inside
     it: a decode forward has no separate merge launch; workloads with rows
@@ -267,31 +268,41 @@ def test_merge_launch_only_when_wide_partials(name, rows, launch):
         assert stats["workspace_bytes"] == 0
 
 
-@pytest.mark.parametrize("name,chains", [("prefill_32k", True), ("join_8000_32k", None), ("fanout_8x20_32k", False),
+@pytest.mark.parametrize("name,chains", [("prefill_32k", True), ("join_8000_32k", True), ("fanout_8x20_32k", False),
                                          ("join_400_32k", False)])
 def test_shards_of_an_m_tile_chain_when_work_is_plentiful(name, chains):
     """With at least two (unit, KV head, M-tile) jobs per workgroup the live
     shards of each job form a chain: consecutive items of one workgroup, in
     shard order over contiguous keys, the first handing its state on, the
-    last writing it, those between doing both. With fewer jobs (fan-out,
+    last writing it, those between doing both. A group with one branch
+    chains the prefix's shards on into the suffix's (same KV head and rows),
+    so the 8000-token join writes every row once. With fewer jobs (fan-out,
     400-token join) no item chains."""
     w = get_workload(name)
-    items, splits, _ = _plan(w)
+    items, splits, stats = _plan(w)
     wide = [it for it in items if it[7] == 0]
     chained = [it for it in wide if it[9]]
     if chains is False:
         assert not chained
         return
-    if chains and splits[0] > 1:
-        assert chained
+    assert chained
+    if name == "join_8000_32k":
+        assert stats["n_merge_rows"] == 0 and stats["workspace_bytes"] == 0
+        assert all(it[9] for it in wide)
     for b in {it[8] for it in wide}:
         for job in _jobs([it for it in wide if it[8] == b]):
             if len(job) == 1:
                 assert job[0][9] == 0
                 continue
-            assert [it[6] for it in job] == list(range(len(job)))                  # shard order
-            assert len({(it[0], it[1], it[2]) for it in job}) == 1                 # one unit, head, M-tile
-            assert all(a[5] == b[4] for a, b in zip(job, job[1:]))                 # contiguous keys
+            assert len({(it[1], it[2], it[3]) for it in job}) == 1                 # one head, one M-tile
+            units = [it[0] for it in job]
+            assert units == sorted(units) and len(set(units)) <= 2
+            if len(set(units)) == 2:                                               # prefix then suffix
+                assert units[0] == 0 and units[-1] == 1 and len(w.branches) == 1
+            for u in set(units):
+                part = [it for it in job if it[0] == u]
+                assert [it[6] for it in part] == list(range(len(part)))            # shard order
+                assert all(a[5] == b[4] for a, b in zip(part, part[1:]))           # contiguous keys
             assert job[0][9] == 2 and job[-1][9] == 1 and all(it[9] == 3 for it in job[1:-1])
 
 

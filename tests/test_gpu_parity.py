@@ -311,6 +311,28 @@ def test_chained_shards_prefill(dtype, d, n, splits):
     H.compare(w, o, lse, ref[0], ref[1], ref[2], label=f"{w.name} ({len(toks)}/{n} tokens)")
 
 
+@pytest.mark.parametrize("dtype,d,n_shared,n,splits", [("bf16", 128, 3000, 2048, [2, 2]),
+                                                        ("fp32", 64, 1500, 1024, [1, 3])])
+def test_chained_join_prefix_into_suffix(dtype, d, n_shared, n, splits):
+    """A join: one branch of n new tokens over an n_shared-token prefix, with
+    jobs enough to chain. Each (KV head, M-tile) chain runs the prefix's
+    shards and then the suffix's, so the state crosses from the shared keys
+    to the paged ones in registers and every row is written once (no
+    partials, no merge launch). Compared with the oracle on every 8th token
+    plus the M-tile and shard edges."""
+    w = custom(f"chain_join_{dtype}", dtype=dtype, H_q=64, H_kv=8, d=d, shared=(n_shared,), branches=((0, n, n),),
+               seed=132, splits=splits)
+    inp = generate(w, "cuda")
+    o, lse, h = H.run_library(w, inp)
+    st = h.plan_stats()
+    H.say(f"  {w.name}: plan {st}")
+    assert st["merge_launch"] == 0 and st["n_merge_rows"] == 0 and st["workspace_bytes"] == 0
+    m_tile = (256 if dtype == "bf16" else 128) // 8
+    toks = sorted(set(range(0, n, 8)) | _edges(n, -(-n // splits[1]), m_tile))
+    ref = H.oracle_rows(w, inp, tokens=toks)
+    H.compare(w, o, lse, ref[0], ref[1], ref[2], label=f"{w.name} ({len(toks)}/{n} tokens)")
+
+
 # ------------------------------------------------ full-size configurations --
 def _parity(name, tokens=None):
     """The library's output at a full-size workload against the oracle on
