@@ -50,7 +50,10 @@ CLOCK_WARMUP_S = 0.3            # untimed sustained load before each timed regio
 WORKLOADS = {"fanout": "fanout_8x20_32k", "decode": "decode_8k", "prefill": "prefill_32k",
              "mixed": "mixed_32dec_64x4", "tiny": "tiny_fp32_fanout", "join400": "join_400_32k",
              "join8000": "join_8000_32k"}
-KERNEL_SOURCES = ["gqa_attention_agentic_amd/csrc/attention.hip"]
+# The attention kernels and the planner that lays out their work: HBM traffic
+# depends on both (shard counts, M-tiles, chains, XCD placement).
+KERNEL_SOURCES = ["gqa_attention_agentic_amd/csrc/attention.hip", "gqa_attention_agentic_amd/csrc/plan.cpp",
+                  "gqa_attention_agentic_amd/csrc/plan_types.h"]
 APPEND_SOURCES = ["gqa_attention_agentic_amd/csrc/append.hip"]
 
 
