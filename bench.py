@@ -529,7 +529,8 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, last: int, cm
     ws, write = read(write_csv, "WRITE_SIZE")
     short = lambda n: n.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1]
     per_kernel = {short(n): {"fetch_bytes": round(fetch[n]), "write_bytes": round(write.get(n, 0.0))} for n in fetch}
-    attn = [k for k in per_kernel if k.startswith("attn_")]
+    # the kernels the roofline's time covers: the attention launches and the merge
+    attn = [k for k in per_kernel if k.startswith("attn_") or k.startswith("lse_merge")]
     w = get_workload(WORKLOADS[workload])
     out = {"workload": w.name, "kernel_hash": kernel_hash(),
            "hbm_bytes_per_launch": sum(per_kernel[k]["fetch_bytes"] + per_kernel[k]["write_bytes"] for k in attn),

@@ -146,9 +146,9 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     as the counter does on this chip): the fetch scale is then 2, and the
     attention kernel's 1000 KiB become 2,048,000 bytes."""
     fetch = [(1, COPY, "FETCH_SIZE", float(1 << 19), 0, 1), (2, ATTN, "FETCH_SIZE", 1000.0, 0, 1),
-             (3, ATTN, "FETCH_SIZE", 1000.0, 0, 1)]
+             (3, ATTN, "FETCH_SIZE", 1000.0, 0, 1), (4, MERGE, "FETCH_SIZE", 50.0, 0, 1)]
     write = [(1, COPY, "WRITE_SIZE", float(1 << 20), 0, 1), (2, ATTN, "WRITE_SIZE", 10.0, 0, 1),
-             (3, ATTN, "WRITE_SIZE", 30.0, 0, 1)]
+             (3, ATTN, "WRITE_SIZE", 30.0, 0, 1), (4, MERGE, "WRITE_SIZE", 5.0, 0, 1)]
     fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
     _pmc_csv(fp, fetch)
     _pmc_csv(wp, write)
@@ -163,5 +163,8 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     k = t["per_kernel"]["attn_wide_dma<128>"]
     assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
     assert k["fetch_bytes"] == 2_048_000 and k["write_bytes"] == 20 * 1024
-    assert t["hbm_bytes_per_launch"] == 2_048_000 + 20 * 1024
+    m = t["per_kernel"]["lse_merge<unsigned short, 128, 8>"]
+    assert m["fetch_bytes"] == 102_400 and m["write_bytes"] == 5 * 1024
+    # the roofline's time covers the attention launches and the merge, and so do its bytes
+    assert t["hbm_bytes_per_launch"] == 2_048_000 + 20 * 1024 + 102_400 + 5 * 1024
     assert t["kernel_hash"] == bench.kernel_hash() and t["command_fetch"] == "cmd-f"
