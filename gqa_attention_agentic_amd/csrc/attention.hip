@@ -968,24 +968,39 @@ __device__ __forceinline__ void dma_tile_any(const KvSrc<uint16_t>& src, const D
 // chunk n + 1 are issued between chunk n's MFMAs (scheduling fences keep
 // the compiler from regrouping them), so the softmax VALU work runs in the
 // matrix core's shadow.
-template <class C, int D, bool MASK>
-__device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const DmaLane<C>& L,
+// Lane bases of the wide kernel's operand reads in its contiguous ring.
+template <class C>
+struct RingLane {
+  uint32_t kaddr[C::QF];   // LDS address of the K operand chunk for ks in stage 0 (this lane)
+  uint32_t vaddr[C::OB];   // LDS address of the V tr16 read for db in stage 0 (this lane)
+};
+
+template <class C, int D, bool MASK, int STAGE = -1, class LA = DmaLane<C>>
+__device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const LA& L,
                                             State<C>& s, int kpos0, int n_valid, int causal,
                                             int row_pos, float c, int i, int h) {
   constexpr float kTau = 8.f;
   typedef __attribute__((address_space(3))) const bf16x8_t* lds_bf16x8;
   typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16;
-  // Per-call opaque bases: every operand address below is base + immediate.
   uint32_t kbs[C::QF], vbs[C::OB];
+  if constexpr (STAGE >= 0) {
+    // Lane bases fixed for the whole launch; the stage is an immediate offset.
 #pragma unroll
-  for (int q = 0; q < C::QF; ++q) {
-    kbs[q] = kst + L.kaddr[q];
-    asm volatile("" : "+v"(kbs[q]));
-  }
+    for (int q = 0; q < C::QF; ++q) kbs[q] = L.kaddr[q] + STAGE * C::TB;
 #pragma unroll
-  for (int q = 0; q < C::OB; ++q) {
-    vbs[q] = vst + L.vaddr[q];
-    asm volatile("" : "+v"(vbs[q]));
+    for (int q = 0; q < C::OB; ++q) vbs[q] = L.vaddr[q] + STAGE * C::TB;
+  } else {
+    // Per-call opaque bases: every operand address below is base + immediate.
+#pragma unroll
+    for (int q = 0; q < C::QF; ++q) {
+      kbs[q] = kst + L.kaddr[q];
+      asm volatile("" : "+v"(kbs[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < C::OB; ++q) {
+      vbs[q] = vst + L.vaddr[q];
+      asm volatile("" : "+v"(vbs[q]));
+    }
   }
   f32x16_t sacc[C::SB];
 #pragma unroll
@@ -1081,6 +1096,19 @@ __device__ __forceinline__ void dma_step(uint32_t kst, uint32_t vst, const DmaLa
   else dma_compute<C, D, false>(kst, vst, L, s, kpos0, nvalid, causal, row_pos, c, i, h);
 }
 
+// The same for a tile in stage STAGE of the wide kernel's contiguous ring.
+template <class C, int D, int STAGE>
+__device__ __forceinline__ void dma_step_ring(const RingLane<C>& R, State<C>& s, int key_pos0, int tk0, int key_end,
+                                              int causal, int row_pos, int pmin, int pmax, bool active, float c,
+                                              int i, int h) {
+  const int kpos0 = key_pos0 + tk0;
+  if (!active || (causal && kpos0 > pmax)) return;
+  const int nvalid = min(C::BN, key_end - tk0);
+  const bool need_mask = (nvalid < C::BN) || (causal && kpos0 + C::BN - 1 > pmin);
+  if (need_mask) dma_compute<C, D, true, STAGE, RingLane<C>>(0, 0, R, s, kpos0, nvalid, causal, row_pos, c, i, h);
+  else dma_compute<C, D, false, STAGE, RingLane<C>>(0, 0, R, s, kpos0, nvalid, causal, row_pos, c, i, h);
+}
+
 
 // Four ring stages consumed two tiles per barrier: after the barrier of pair
 // p (tiles 2p, 2p+1) the DMA of pair p+1 is issued into the two stages the
@@ -1091,16 +1119,32 @@ template <int D>
 __global__ void __launch_bounds__(DmaCfg<D>::THREADS, 2)
 attn_wide_dma(AttnArgs a) {
   using C = DmaCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char k0[C::TB];
-  __shared__ __attribute__((aligned(1024))) char v0[C::TB];
-  __shared__ __attribute__((aligned(1024))) char k1[C::TB];
-  __shared__ __attribute__((aligned(1024))) char v1[C::TB];
-  __shared__ __attribute__((aligned(1024))) char k2[C::TB];
-  __shared__ __attribute__((aligned(1024))) char v2[C::TB];
-  __shared__ __attribute__((aligned(1024))) char k3[C::TB];
-  __shared__ __attribute__((aligned(1024))) char v3[C::TB];
+  // The ring: K stages 0..3, then V stages 0..3. Kept contiguous so that
+  // every operand address is a lane base fixed for the launch plus an
+  // immediate (the stage is known at compile time in the unrolled loop):
+  // no per-tile address arithmetic.
+  __shared__ __attribute__((aligned(1024))) char ring[8 * C::TB];
+  char* const k0 = ring;
+  char* const k1 = ring + C::TB;
+  char* const k2 = ring + 2 * C::TB;
+  char* const k3 = ring + 3 * C::TB;
+  char* const v0 = ring + 4 * C::TB;
+  char* const v1 = ring + 5 * C::TB;
+  char* const v2 = ring + 6 * C::TB;
+  char* const v3 = ring + 7 * C::TB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const DmaLane<C> L = dma_lane<C>(wave, lane);
+  RingLane<C> R;
+#pragma unroll
+  for (int q = 0; q < C::QF; ++q) {
+    R.kaddr[q] = lds_u32(ring) + L.kaddr[q];
+    asm volatile("" : "+v"(R.kaddr[q]));
+  }
+#pragma unroll
+  for (int q = 0; q < C::OB; ++q) {
+    R.vaddr[q] = lds_u32(ring) + 4 * C::TB + L.vaddr[q];
+    asm volatile("" : "+v"(R.vaddr[q]));
+  }
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
   State<C> s;   // carried from one item to the next along a chain
   for (int idx = bin_begin; idx < bin_end; ++idx) {
@@ -1124,29 +1168,29 @@ attn_wide_dma(AttnArgs a) {
     wave_pos_range(w, &pmin, &pmax);
     const bool active = wave * 32 < it.n_rows;
     const float c = a.scale_log2;
-#define GQA_DMA_PAIR(KA, VA, KB, VB, KN0, VN0, KN1, VN1)                                                    \
+#define GQA_RING_PAIR(SA, KN0, VN0, KN1, VN1)                                                               \
     {                                                                                                       \
       wait_dma<0>();                                                                                        \
       lds_barrier();                                                                                        \
       if (j + 2 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 2) * C::BN, ke, KN0, VN0);                \
       if (j + 3 < nt) dma_tile_any<C, D>(src, L, wave, kb0 + (j + 3) * C::BN, ke, KN1, VN1);                \
-      dma_step<C, D>(lds_u32(KA), lds_u32(VA), L, s, it.key_pos0, kb0 + j * C::BN, ke, a.causal, w.pos, pmin,    \
-                     pmax, active, c, i, h);                                                                \
+      dma_step_ring<C, D, SA>(R, s, it.key_pos0, kb0 + j * C::BN, ke, a.causal, w.pos, pmin, pmax, active,  \
+                              c, i, h);                                                                     \
       if (j + 1 < nt)                                                                                       \
-        dma_step<C, D>(lds_u32(KB), lds_u32(VB), L, s, it.key_pos0, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, \
-                       pmin, pmax, active, c, i, h);                                                        \
+        dma_step_ring<C, D, SA + 1>(R, s, it.key_pos0, kb0 + (j + 1) * C::BN, ke, a.causal, w.pos, pmin,    \
+                                    pmax, active, c, i, h);                                                 \
     }
     for (int j0 = 0; j0 < nt; j0 += 4) {
       {
         const int j = j0;
-        GQA_DMA_PAIR(k0, v0, k1, v1, k2, v2, k3, v3)
+        GQA_RING_PAIR(0, k2, v2, k3, v3)
       }
       if (j0 + 2 < nt) {
         const int j = j0 + 2;
-        GQA_DMA_PAIR(k2, v2, k3, v3, k0, v0, k1, v1)
+        GQA_RING_PAIR(2, k0, v0, k1, v1)
       }
     }
-#undef GQA_DMA_PAIR
+#undef GQA_RING_PAIR
     if (!(it.chain & kChainContinued)) {
       s.l += __shfl_xor(s.l, 32);   // the two half-rows' sums, once per result
       write_row<C, uint16_t, D>(a, it, w, rloc, s.m, s.l, s.o, 0, C::OB, true, h);
