@@ -1024,11 +1024,14 @@ __device__ __forceinline__ void dma_compute(uint32_t kst, uint32_t vst, const LA
       for (int r = 0; r < 16; ++r)
         sacc[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3) < lim) ? sacc[kb][r] : kNegInf;
   }
+  // A chain of two-input maxima, which the compiler fuses pairwise into
+  // v_max3_f32: one instruction per two scores (16 per tile, against 24
+  // when each pair is reduced first).
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < C::SB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sacc[kb][r]), sacc[kb][r + 1]);
   // Lane-local max over its half of the row's keys: the rescale decision
   // needs no exchange (the ballot spans the wave); only an actual rescale
   // combines the two halves' maxima, so both keep the same m.
