@@ -63,7 +63,8 @@ struct BranchDesc {
 // for the tile (shards are in key order and liveness under causality is a
 // prefix), and where the tile's partials start in the workspace.
 struct TileInfo {
-  int32_t live;        // partials per row from this tile: its live shards, or 1 when they form chains
+  int32_t live;        // partials per row from this tile: its live shards, 1 when they form a chain,
+                       // 0 when its chain continues into the suffix unit
   int64_t part_off;    // first partial row (-1: none); row layout ((kv * live + s) * bm + r_in_tile)
 };
 
@@ -89,7 +90,9 @@ struct WorkItem {
 
 // WorkItem::chain bits. The shards of one (unit, KV head, M-tile) may form a
 // chain: the items run back to back in one workgroup, in shard order, and
-// the rows' (m, l, O) state passes from one to the next in registers.
+// the rows' (m, l, O) state passes from one to the next in registers. In a
+// group with a single branch, a prefix tile's chain continues into the
+// shards of the same rows' suffix tile.
 constexpr int32_t kChainContinues = 1;   // starts from the previous item's state (no Q load)
 constexpr int32_t kChainContinued = 2;   // hands its state to the next item (no write)
 

@@ -296,7 +296,8 @@ gqa_status gqa_attn_append_times(gqa_attn* h, double* ms, int64_t* n_calls);
  * `chain` is 0 for an item on its own; otherwise bit 0 says the item starts
  * from the previous item's (m, l, O) state and bit 1 that it hands its state
  * to the next item instead of writing it (the shards of one M-tile and KV
- * head run back to back, merged in registers).
+ * head run back to back, merged in registers; in a group with a single
+ * branch the prefix's chain continues into the same rows' suffix shards).
  * Returns the item count through *n_items and the per-unit split counts
  * through `splits` (host, n_groups + n_branches entries, may be NULL). */
 gqa_status gqa_attn_plan_host(const gqa_attn_params* p,
