@@ -103,6 +103,50 @@ def test_small_parity(name):
     H.full_parity(SMALL[name]())
 
 
+def _random_workload(seed):
+    """A seeded random configuration small enough for the oracle: 1-2
+    groups, 1-4 branches each, any G, d, page size and causality, and the
+    split counts either the heuristic's or random. Every branch's new tokens
+    are at most its context."""
+    import random
+    r = random.Random(seed)
+    dtype = "fp32" if r.random() < 0.2 else "bf16"
+    H_kv = r.choice([1, 2, 4])
+    G = r.choice([1, 2, 3, 4, 8])
+    d = r.choice([64, 128])
+    ps = r.choice([1, 4, 8, 12, 16, 32])
+    n_groups = r.choice([1, 1, 2])
+    shared = tuple(r.choice([0, r.randint(1, 700)]) for _ in range(n_groups))
+    branches = []
+    for g in range(n_groups):
+        for _ in range(r.randint(1, 4)):
+            priv = r.choice([0, r.randint(1, 300)])
+            ctx = shared[g] + priv
+            if ctx == 0:
+                priv, ctx = 5, shared[g] + 5
+            branches.append((g, r.randint(0, min(40, ctx)), priv))
+    splits = None
+    if r.random() < 0.5:
+        splits = [r.randint(1, 9) for _ in range(n_groups + len(branches))]
+    return custom(f"random_{seed}", dtype=dtype, H_q=H_kv * G, H_kv=H_kv, d=d, page_size=ps, shared=shared,
+                  branches=tuple(branches), causal=r.random() < 0.8, seed=1000 + seed, splits=splits)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    """Seeded random shapes across the planner's and kernels' paths (both
+    attention kernels, paged and shared sources, ragged tiles, empty
+    branches, forced and heuristic shards), every output against the
+    oracle."""
+    w = _random_workload(seed)
+    H.say(f"  {w.name}: {w.dtype} H_q {w.num_q_heads} H_kv {w.num_kv_heads} d {w.head_dim} ps {w.page_size} "
+          f"groups {[g.shared_len for g in w.groups]} branches {[(b.group, b.q_len, b.private_len) for b in w.branches]} "
+          f"causal {w.causal} splits {w.splits}")
+    if sum(b.q_len for b in w.branches) == 0:
+        pytest.skip("no query tokens drawn")
+    H.full_parity(w)
+
+
 @pytest.mark.parametrize("splits", [[4, 2, 1, 3], [1, 1, 1, 1], [16, 5, 4, 9]])
 def test_split_override(splits):
     w = SMALL["fanout_bf16_d128"]()
