@@ -224,10 +224,11 @@ void serialise_plan(const gqa::Plan& P, const PlanLayout& L, char* dst) {
   put(L.combs, P.combs.data(), P.combs.size() * sizeof(gqa::CombTok));
 }
 
-// Bytes of the arrival counters (one per query token and KV head) and of the
-// partial workspace ((m, l) rows, then O rows) that a plan needs.
+// Bytes of the arrival counters (one per token combined in the narrow
+// launch and KV head, a 128-byte line each) and of the partial workspace
+// ((m, l) rows, then O rows) that a plan needs.
 size_t counter_bytes(const gqa::Plan& P, int H_kv) {
-  return P.part_rows ? align_up((size_t)P.n_q_tokens * H_kv * sizeof(int32_t), 256) : 0;
+  return align_up((size_t)P.n_counter_slots * H_kv * gqa::kCounterStride * sizeof(int32_t), 256);
 }
 size_t ml_bytes(const gqa::Plan& P) { return align_up((size_t)P.part_rows * sizeof(float2), 256); }
 size_t work_bytes(const gqa::Plan& P, int D) {

@@ -505,6 +505,47 @@ __device__ __forceinline__ void write_row_to(const AttnArgs& a, const RowDest& d
   }
 }
 
+// The same for the entry groups q0 .. q0 + NQ - 1 of O^T block db, given as
+// float4s (entries 4 q .. 4 q + 3 of the block's accumulator).
+template <typename T, int D, bool COHERENT, int NQ>
+__device__ __forceinline__ void write_row_groups(const AttnArgs& a, const RowDest& dst, bool ok, float m, float l,
+                                                 const float4 (&v)[NQ], int db, int q0, bool write_scalars, int h) {
+  if (!ok) return;
+  if (dst.direct) {
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const int64_t orow = dst.row * D;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int d0 = 32 * db + 8 * (q0 + j) + 4 * h;
+      if constexpr (std::is_same<T, uint16_t>::value) {
+        uint2 pk;
+        pk.x = pack_bf16x2(v[j].x * inv, v[j].y * inv);
+        pk.y = pack_bf16x2(v[j].z * inv, v[j].w * inv);
+        *(uint2*)((uint16_t*)a.o + orow + d0) = pk;
+      } else {
+        *(float4*)((float*)a.o + orow + d0) = make_float4(v[j].x * inv, v[j].y * inv, v[j].z * inv, v[j].w * inv);
+      }
+    }
+    if (write_scalars && h == 0) a.lse[dst.row] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : kNegInf;
+  } else {
+    float* po = a.part_o + dst.row * D;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int d0 = 32 * db + 8 * (q0 + j) + 4 * h;
+      if (COHERENT) {
+        store_device(po + d0, v[j].x, v[j].y);
+        store_device(po + d0 + 2, v[j].z, v[j].w);
+      } else {
+        *(float4*)(po + d0) = v[j];
+      }
+    }
+    if (write_scalars && h == 0) {
+      if (COHERENT) store_device(&a.part_ml[dst.row], m, l);
+      else a.part_ml[dst.row] = make_float2(m, l);
+    }
+  }
+}
+
 template <class C, typename T, int D>
 __device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it, const Row& w, int rloc,
                                           float m, float l, const f32x16_t* o, int db0, int db1,
@@ -588,6 +629,77 @@ __device__ __forceinline__ void write_combined(const AttnArgs& a, int tok, int k
   if (d0 == 0) a.lse[orow] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
+// Folds the partials of row (tok, g) of KV head kv, whose combination
+// record is c, and writes its O and LSE. RL = D / 2 lanes take the row, this
+// one being number j of them (lane0: the first of them in the wave): lanes 2y
+// and 2y + 1 own the row's d values 4y .. 4y + 3, and each folds every other
+// partial. The lanes first take one partial's (m, l) each, so that the row's
+// maximum M, and each partial's weight 2^(m_i - M), are formed once,
+// lane-parallel; the weights reach the O lanes by a lane exchange. The sum
+// runs in a fixed order.
+template <typename T, int D>
+__device__ __forceinline__ void fold_row(const AttnArgs& a, const CombTok& c, int kv, int tok, int g, int j,
+                                         int lane0) {
+  constexpr int RL = D / 2;
+  const int n = c.live[0] + c.live[1];
+  const int half = j & 1, d0 = (j >> 1) * 4;
+  constexpr int U = 8;                      // partial loads in flight per lane
+  // The row's first RL partials' (m, l), one per lane, and this lane's
+  // first U partials' O values go out together: the O loads do not wait
+  // for the weights.
+  float2 ml0 = make_float2(kNegInf, 0.f);
+  if (j < n) ml0 = a.part_ml[part_of(c, kv, g, j)];
+  const int cnt0 = min(RL, n);
+  float4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int kk = 2 * u + half;
+    v[u] = kk < cnt0 ? *(const float4*)(a.part_o + part_of(c, kv, g, kk) * D + d0)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float M = ml0.x;
+  for (int c0 = RL; c0 < n; c0 += RL)
+    if (c0 + j < n) M = fmaxf(M, a.part_ml[part_of(c, kv, g, c0 + j)].x);
+#pragma unroll
+  for (int sh = 1; sh < RL; sh <<= 1) M = fmaxf(M, __shfl_xor(M, sh));
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < n; c0 += RL) {
+    float2 ml = ml0;
+    if (c0 > 0) ml = (c0 + j < n) ? a.part_ml[part_of(c, kv, g, c0 + j)] : make_float2(kNegInf, 0.f);
+    const float wq = exp2_fast(ml.x - Mu);  // 0 for an empty partial (m = -inf)
+    L += wq * ml.y;
+    const int cnt = min(RL, n - c0);
+    for (int t0 = 0; t0 < cnt; t0 += 2 * U) {
+      if (c0 > 0 || t0 > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kk = t0 + 2 * u + half;
+          v[u] = kk < cnt ? *(const float4*)(a.part_o + part_of(c, kv, g, c0 + kk) * D + d0)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = t0 + 2 * u + half;
+        const float wu = __shfl(wq, lane0 + min(kk, cnt - 1)) * (kk < cnt ? 1.f : 0.f);
+        O.x += wu * v[u].x;
+        O.y += wu * v[u].y;
+        O.z += wu * v[u].z;
+        O.w += wu * v[u].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int sh = 1; sh < RL; sh <<= 1) L += __shfl_xor(L, sh);
+  O.x += __shfl_xor(O.x, 1);
+  O.y += __shfl_xor(O.y, 1);
+  O.z += __shfl_xor(O.z, 1);
+  O.w += __shfl_xor(O.w, 1);
+  if (half == 0) write_combined<T, D>(a, tok, kv, g, d0, M, L, O);
+}
+
 // s_waitcnt immediate: vmcnt(vm), expcnt(7), lgkmcnt(0).
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | ((vm >> 4) << 14); }
 
@@ -661,13 +773,13 @@ __device__ __forceinline__ void combine_prepare(const AttnArgs& a, const WorkIte
       c.bm[0] = plan_load(&src->bm[0]);
       c.bm[1] = plan_load(&src->bm[1]);
       c.need = plan_load(&src->need);
-      c.pad = 0;
+      c.slot = plan_load(&src->slot);
     } else {
       c.p[0] = c.p[1] = 0;
       c.live[0] = c.live[1] = 0;
       c.bm[0] = c.bm[1] = 0;
       c.need = 0;
-      c.pad = 0;
+      c.slot = -1;
     }
     if (lane == 0) cl->rec[k] = c;
   }
@@ -685,12 +797,11 @@ __device__ __forceinline__ void combine_if_last(const AttnArgs& a, int tid, Comb
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __syncthreads();
   const int kv = cl->kv, tok0 = cl->tok0, ntok = cl->ntok;
-  int mine = 0;
   for (int k = tid; k < ntok; k += NT) {
     const int need = cl->rec[k].need;
     int w = 0;
     if (need > 0) {
-      int* c = a.counters + (int64_t)(tok0 + k) * a.H_kv + kv;
+      int* c = a.counters + ((int64_t)cl->rec[k].slot * a.H_kv + kv) * kCounterStride;
       if (!a.coherent_parts) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       if (atomicAdd(c, 1) == need - 1) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -698,34 +809,31 @@ __device__ __forceinline__ void combine_if_last(const AttnArgs& a, int tid, Comb
       }
     }
     cl->won[k] = w;
-    mine |= w;
   }
-  if (!__syncthreads_or(mine)) return;
+  // Whether any of the item's tokens is combined here, from the flags in
+  // LDS (a workgroup OR-reduction would compile to a library call, whose
+  // register saves cost the K/V stream loop registers).
+  __syncthreads();
+  int any = 0;
+  for (int k = 0; k < ntok; ++k) any |= cl->won[k];
+  if (!any) return;
   const int G = a.G;
-  constexpr int TPR = D / 4;   // threads (pairs) per row
-  // Lanes 2y and 2y + 1 take (row, d0) number y; the trip count and every
-  // skip below are the same for both lanes of a pair.
-  for (int x = tid; x < 2 * ntok * G * TPR; x += NT) {
-    const int y = x >> 1, half = x & 1;
-    const int rr = y / TPR;
+  constexpr int RL = D / 2;   // lanes per row: two per group of four d values
+  for (int x = tid; x < ntok * G * RL; x += NT) {
+    const int rr = x / RL, j = x - rr * RL;   // row, lane within the row
     const int k = rr / G;
-    if (!cl->won[k]) continue;
-    const CombTok c = cl->rec[k];
-    const int n = c.live[0] + c.live[1];
-    const int g = rr - k * G, d0 = (y - rr * TPR) * 4;
-    const int mid = (n + 1) >> 1;
-    float M = kNegInf, L = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    fold_parts<D, 16>(a, c, kv, g, half ? mid : 0, half ? n : mid, d0, M, L, O);
-    const float M2 = __shfl_xor(M, 1), L2 = __shfl_xor(L, 1);
-    const float4 O2 = make_float4(__shfl_xor(O.x, 1), __shfl_xor(O.y, 1), __shfl_xor(O.z, 1), __shfl_xor(O.w, 1));
-    if (half == 0) {
-      join_state(M, L, O, M2, L2, O2);
-      write_combined<T, D>(a, tok0 + k, kv, g, d0, M, L, O);
-    }
+    if (!cl->won[k]) continue;                // the same for every lane of the row
+    int lane = tid & 63;
+    // Opaque, so that nothing derived from the lane index (the exchange
+    // addresses of the fold) is hoisted out of the item loop and kept live
+    // through the K/V stream.
+    asm volatile("" : "+v"(lane));
+    fold_row<T, D>(a, cl->rec[k], kv, tok0 + k, rr - k * G, j, lane - j);
   }
-  for (int k = tid; k < ntok; k += NT)
-    if (cl->won[k]) atomicExch(a.counters + (int64_t)(tok0 + k) * a.H_kv + kv, 0);
+  int t = tid;
+  asm volatile("" : "+v"(t));   // no LDS address of this loop is computed at the kernel's start and kept
+  for (int k = t; k < ntok; k += NT)
+    if (cl->won[k]) atomicExch(a.counters + ((int64_t)cl->rec[k].slot * a.H_kv + kv) * kCounterStride, 0);
 }
 
 // Smallest / largest valid row position of the wave.
@@ -1307,7 +1415,8 @@ struct NarrowDmaCfg {
   static constexpr int OB = D / 32, QF = D / 16, SB = BN / 32;
   static constexpr int MERGE_O = WAVES * OB * 16 * 64 * 4;   // bytes of the per-wave O^T exchange
   static_assert(WAVES * 2 * TB >= MERGE_O, "the stages must hold the merge exchange");
-  static_assert(OB <= WAVES, "one wave per O^T block in the final combination");
+  static_assert(WAVES % OB == 0 && 4 % (WAVES / OB) == 0,
+                "the waves split the O^T blocks' entry groups evenly in the final combination");
 };
 
 template <int D>
@@ -1352,18 +1461,27 @@ attn_narrow_dma(AttnArgs a) {
         dma_tile_any<C, D>(src, L, 0, kb0 + (j + C::WAVES) * C::BN, ke, K0, V0);
       }
     }
-    // Merge the eight waves' states (same rows, disjoint keys) through LDS.
+    // Merge the eight waves' states (same rows, disjoint keys) through LDS:
+    // only the lanes of the item's rows take part (a decode fills 8 of the
+    // tile's 32), four accumulator entries per LDS access, and every wave
+    // combines a quarter or half of one O^T block.
     s.l += __shfl_xor(s.l, 32);
     wait_dma<0>();
     __syncthreads();
-    float* mo = (float*)st;                       // [wave][db][r][lane]
+    float4* mo = (float4*)st;                     // [wave][db][group of 4 entries][lane]
+    if (w.ok) {
 #pragma unroll
-    for (int db = 0; db < C::OB; ++db)
+      for (int db = 0; db < C::OB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mo[((wave * C::OB + db) * 16 + r) * 64 + lane] = s.o[db][r];
+        for (int r4 = 0; r4 < 4; ++r4)
+          mo[((wave * C::OB + db) * 4 + r4) * 64 + lane] =
+              make_float4(s.o[db][4 * r4], s.o[db][4 * r4 + 1], s.o[db][4 * r4 + 2], s.o[db][4 * r4 + 3]);
+    }
     mml[wave * 64 + lane] = make_float2(s.m, s.l);
     __syncthreads();
-    if (wave < C::OB) {
+    {
+      constexpr int WPB = C::WAVES / C::OB, NQ = 4 / WPB;   // waves per O^T block, entry groups per wave
+      const int db = wave / WPB, q0 = (wave % WPB) * NQ;
       float mk[C::WAVES], lk[C::WAVES];
       float M = kNegInf;
 #pragma unroll
@@ -1380,19 +1498,24 @@ attn_narrow_dma(AttnArgs a) {
         wk[k] = exp2_fast(mk[k] - M_use);
         Lsum += lk[k] * wk[k];
       }
-      const int db = wave;
-      f32x16_t acc;
+      float4 acc[NQ];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = 0.f;
+      for (int j = 0; j < NQ; ++j) {
+        acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!w.ok) continue;
 #pragma unroll
-        for (int k = 0; k < C::WAVES; ++k) x += wk[k] * mo[((k * C::OB + db) * 16 + r) * 64 + lane];
-        acc[r] = x;
+        for (int k = 0; k < C::WAVES; ++k) {
+          const float4 v = mo[((k * C::OB + db) * 4 + q0 + j) * 64 + lane];
+          acc[j].x += wk[k] * v.x;
+          acc[j].y += wk[k] * v.y;
+          acc[j].z += wk[k] * v.z;
+          acc[j].w += wk[k] * v.w;
+        }
       }
       if (a.coherent_parts)
-        write_row_to<C, uint16_t, D, true>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
+        write_row_groups<uint16_t, D, true>(a, dst, w.ok, M, Lsum, acc, db, q0, wave == 0, h);
       else
-        write_row_to<C, uint16_t, D>(a, dst, w.ok, M, Lsum, &acc, db, db + 1, wave == 0, h);
+        write_row_groups<uint16_t, D, false>(a, dst, w.ok, M, Lsum, acc, db, q0, wave == 0, h);
     }
     combine_if_last<uint16_t, D, C::THREADS>(a, tid, &cl);
   }

@@ -657,6 +657,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
   // number of such items per KV head); any other goes to the merge kernel.
   P->tok_rec.assign(P->n_q_tokens, TokRec{0, -1});
   P->combs.clear();
+  P->n_counter_slots = 0;
   for (int32_t b = 0; b < nb; ++b) {
     const BranchDesc& br = P->branches[b];
     for (int32_t t = 0; t < br.q_len; ++t) {
@@ -682,6 +683,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       if (n < 2) continue;
       P->merge_rows += (int64_t)G * in.H_kv;
       c.need = narrow_only ? n : 0;
+      c.slot = narrow_only ? P->n_counter_slots++ : -1;
       if (!narrow_only) P->merge_launch = true;
       tr.comb = (int32_t)P->combs.size();
       P->combs.push_back(c);

@@ -44,6 +44,7 @@ struct Plan {
   int32_t max_row_parts = 0;        // largest partial count of any output row
   std::vector<TokRec> tok_rec;      // per query token
   std::vector<CombTok> combs;       // per token whose rows have two or more partials
+  int32_t n_counter_slots = 0;      // tokens combined in the narrow launch (CombTok::slot)
   bool merge_launch = false;        // some row is left to the separate merge kernel
   // Both kernels have items and run side by side on disjoint sets of compute
   // units (wide_cus + narrow_cus = the device's); else each gets all of them.

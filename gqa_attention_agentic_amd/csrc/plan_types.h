@@ -114,7 +114,13 @@ struct CombTok {
   int32_t live[2];
   int32_t bm[2];
   int32_t need;
-  int32_t pad;
+  int32_t slot;        // need > 0: the token's arrival counters, one per KV head, are
+                       // counters[(slot * H_kv + kv) * kCounterStride]; -1 otherwise
 };
+
+// Distance in 32-bit words between two arrival counters: one 128-byte line
+// each, so that the atomics of different (token, KV head) pairs, which all
+// land within a few microseconds of each other, do not queue on one line.
+constexpr int kCounterStride = 32;
 
 }  // namespace gqa

@@ -162,8 +162,10 @@ gqa_status gqa_attn_forward(gqa_attn* h,
  *    hipHostMalloc and no allocating library call; the host planner uses
  *    ordinary heap memory when the metadata changes.
  *  - A forward whose plan and partials do not fit returns
- *    GQA_ERR_NO_MEMORY before any launch (n_q_tokens x H_kv counters must
- *    fit 1 MiB; plan + partial rows x (d + 2) x 4 bytes the rest). The
+ *    GQA_ERR_NO_MEMORY before any launch (a 128-byte counter per KV head for
+ *    each token combined inside the decode-class launch -- 1024 such tokens
+ *    at 8 KV heads -- must fit 1 MiB; plan + partial rows x (d + 2) x 4
+ *    bytes the rest). The
  *    fan-out and decode workloads fit; a long prefill split into many
  *    shards does not -- use gqa_attn_forward for it.
  *  - Every call on one GPU, from any handle, shares that GPU's array, which

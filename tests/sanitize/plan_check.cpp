@@ -182,7 +182,23 @@ void check_plan(const std::string& name, const PlanInput& in, const Plan& P) {
     branch_pairs += (int64_t)(in.causal ? tok_pos[tok] + 1 : C) * G * in.H_kv;
   }
   expect(branch_pairs == expected, name + ": units cover each branch's whole context");
-  // combination records
+  // combination records; the tokens combined in the narrow launch each own
+  // one arrival-counter slot, and no two share one
+  std::vector<int> slot_owner(P.n_counter_slots, -1);
+  for (int ci = 0; ci < (int)P.combs.size(); ++ci) {
+    const CombTok& c = P.combs[ci];
+    if (c.need > 0) {
+      const bool in_range = c.slot >= 0 && c.slot < P.n_counter_slots;
+      expect(in_range, name + ": counter slot in range");
+      if (in_range) {
+        expect(slot_owner[c.slot] < 0, name + ": counter slot used once");
+        slot_owner[c.slot] = ci;
+      }
+    } else {
+      expect(c.slot == -1, name + ": no counter slot for a token the merge kernel combines");
+    }
+  }
+  for (int x = 0; x < P.n_counter_slots; ++x) expect(slot_owner[x] >= 0, name + ": every counter slot used");
   for (int tok = 0; tok < ntok; ++tok) {
     const int ci = P.tok_rec[tok].comb;
     for (int kv = 0; kv < in.H_kv; ++kv) {

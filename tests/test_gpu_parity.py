@@ -92,6 +92,17 @@ SMALL = {
     "decodes_several_items_per_workgroup": lambda: custom(
         "decodes_several_items_per_workgroup", shared=(0,), branches=tuple((0, 1, 1500 + 37 * k) for k in range(48)),
         seed=127, splits=[0] + [4] * 48),
+    # Decode-shaped tokens combined inside the narrow launch, past the fold's
+    # first 64 partials (d = 128: one row per wave; d = 64: two rows per
+    # wave), and with partials from both a prefix and a suffix unit.
+    "decode_bf16_100_shards": lambda: custom("decode_bf16_100_shards", shared=(12800,), branches=((0, 1, 0),),
+                                             causal=False, seed=133, splits=[100, 0]),
+    "decode_bf16_d64_70_shards": lambda: custom("decode_bf16_d64_70_shards", d=64, shared=(7000,),
+                                                branches=((0, 1, 0),), causal=False, seed=134, splits=[70, 0]),
+    "decode_two_units_d128": lambda: custom("decode_two_units_d128", shared=(2000,), branches=((0, 1, 300),),
+                                            seed=135, splits=[5, 3]),
+    "decode_two_units_d64": lambda: custom("decode_two_units_d64", d=64, shared=(1500,), branches=((0, 1, 400),),
+                                           seed=136, splits=[4, 6]),
     # Non-causal multi-token queries: every key of the context is visible.
     "noncausal_fanout": lambda: custom("noncausal_fanout", shared=(300,), branches=((0, 5, 40), (0, 7, 21)),
                                        causal=False, seed=126),
