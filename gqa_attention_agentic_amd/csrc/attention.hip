@@ -726,8 +726,10 @@ __device__ __forceinline__ T plan_load(const T* p) {
 //    the narrow kernel only when all its rows fit one M-tile, so an item
 //    has at most BM rows and tokens).
 //  * After its rows are written, each such token's counter (one per KV
-//    head) is incremented; the item that brings it to the planned number of
-//    arrivals combines the token's rows. The XCDs' L2 caches are not
+//    head, in the token's counter slot, a 128-byte line apart from every
+//    other counter so that the items of different KV heads and tokens do
+//    not queue their atomics on one line) is incremented; the item that
+//    brings it to the planned number of arrivals combines the token's rows. The XCDs' L2 caches are not
 //    coherent with each other, so every other item's partials must reach
 //    device scope before its increment, and the winner acquires at device
 //    scope after its own. Two ways:
@@ -743,9 +745,10 @@ __device__ __forceinline__ T plan_load(const T* p) {
 //    The winner resets the counter after its combination, so all counters
 //    are zero again when the launch ends. Work per workgroup is bounded and
 //    no thread waits on another workgroup.
-//  * Two threads share each (row, 4 d values): each folds one half of the
-//    row's partials, so a decode row's shards arrive in one round of loads,
-//    and the halves are joined through a lane exchange.
+//  * The fold of a row (fold_row) takes D / 2 lanes: two per group of four
+//    d values, each summing every other partial, joined by a lane exchange
+//    at the end. Its cost is the bytes of the row's partials passing
+//    through one CU's vector-memory path.
 template <int BM>
 struct CombLds {
   CombTok rec[BM];   // per token of the item (need = 0: combined elsewhere, or one partial)
