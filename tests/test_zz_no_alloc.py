@@ -146,3 +146,29 @@ def test_noalloc_refuses_what_does_not_fit():
     _check(small, si, ref, got, "after the refusal")
     h.close()
     h2.close()
+
+
+def test_noalloc_refuses_more_counters_than_its_region():
+    """513 one-token decodes at 16 KV heads, each combined inside the launch
+    from 2 shards, need a 128-byte arrival counter per (token, KV head):
+    1.05 MB, past the scratch's 1 MiB counter region. The no-allocation call
+    refuses before any launch; gqa_attn_forward runs the same forward, and
+    three of its branches are checked against the oracle."""
+    w = custom("na_too_many_counters", H_q=16, H_kv=16, d=64, shared=(0,),
+               branches=tuple((0, 1, 64) for _ in range(513)), seed=208, splits=[0] + [2] * 513)
+    inp = generate(w, "cuda")
+    h = H.handle_for(w)
+    out = torch.full_like(inp.q, SENTINEL)
+    lse = torch.full((inp.q.shape[0], w.num_q_heads), SENTINEL, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    st, msg = _call(h, "gqa_attn_forward_noalloc", inp, w.causal, out, lse, splits=w.splits)
+    H.say(f"  too many counters: status {st}, '{msg}'")
+    assert st == _lib.GQA_ERR_NO_MEMORY and "counter" in msg, (st, msg)
+    torch.cuda.synchronize()
+    assert bool((out == SENTINEL).all()) and bool((lse == SENTINEL).all())
+    st, msg = _call(h, "gqa_attn_forward", inp, w.causal, out, lse, splits=w.splits)
+    assert st == _lib.GQA_OK, msg
+    torch.cuda.synchronize()
+    o_ref, l_ref, toks = H.oracle_rows(w, inp, branches=[0, 256, 512])
+    H.compare(w, out, lse, o_ref, l_ref, toks, label="513 combined tokens, owned workspace")
+    h.close()
