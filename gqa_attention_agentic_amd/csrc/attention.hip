@@ -567,9 +567,9 @@ __device__ __forceinline__ void write_row(const AttnArgs& a, const WorkItem& it,
 __device__ __forceinline__ int64_t part_of(const CombTok& c, int kv, int g, int q) {
   const bool pre = q < c.live[0];
   const int64_t p = pre ? c.p[0] : c.p[1];
-  const int live = pre ? c.live[0] : c.live[1], bm = pre ? c.bm[0] : c.bm[1];
+  const int live = pre ? c.live[0] : c.live[1], stride = pre ? c.stride[0] : c.stride[1];
   const int sh = pre ? q : q - c.live[0];
-  return p + ((int64_t)kv * live + sh) * bm + g;
+  return p + ((int64_t)kv * live + sh) * stride + g;
 }
 
 // (M, L, O) <- the combination of (M, L, O) and (M2, L2, O2), in that order.
@@ -773,14 +773,14 @@ __device__ __forceinline__ void combine_prepare(const AttnArgs& a, const WorkIte
       c.p[1] = plan_load(&src->p[1]);
       c.live[0] = plan_load(&src->live[0]);
       c.live[1] = plan_load(&src->live[1]);
-      c.bm[0] = plan_load(&src->bm[0]);
-      c.bm[1] = plan_load(&src->bm[1]);
+      c.stride[0] = plan_load(&src->stride[0]);
+      c.stride[1] = plan_load(&src->stride[1]);
       c.need = plan_load(&src->need);
       c.slot = plan_load(&src->slot);
     } else {
       c.p[0] = c.p[1] = 0;
       c.live[0] = c.live[1] = 0;
-      c.bm[0] = c.bm[1] = 0;
+      c.stride[0] = c.stride[1] = 0;
       c.need = 0;
       c.slot = -1;
     }

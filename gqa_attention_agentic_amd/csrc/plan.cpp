@@ -605,12 +605,14 @@ std::string build_plan(const PlanInput& in, Plan* P) {
       TileInfo& ti = P->tiles[u.tile_off + t];
       const int32_t live = shards_live[u.tile_off + t];   // items of the tile per KV head
       const int32_t parts = ti.live;                      // partials of the tile per KV head
-      if (tile_needs[u.tile_off + t]) {
-        ti.part_off = part;
-        part += (int64_t)in.H_kv * parts * u.bm;
-      }
       const int32_t row_begin = uw[ui].tile_tok[t] * G;
       const int32_t n_rows = (uw[ui].tile_tok[t + 1] - uw[ui].tile_tok[t]) * G;
+      // A tile's partials are packed at its own row count: rows of the
+      // kernel's M-tile past the tile's rows get no workspace.
+      if (tile_needs[u.tile_off + t]) {
+        ti.part_off = part;
+        part += (int64_t)in.H_kv * parts * n_rows;
+      }
       for (int32_t s = 0; s < live; ++s) {
         for (int32_t kv = 0; kv < in.H_kv; ++kv) {
           WorkItem w{};
@@ -628,7 +630,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
           w.key_pos0 = u.key_pos0;
           // Rows of a tile without workspace rows all write directly; the
           // kernel never uses part_row for them.
-          w.part_row = ti.part_off >= 0 ? ti.part_off + ((int64_t)kv * parts + (chained[ui] ? 0 : s)) * u.bm : 0;
+          w.part_row = ti.part_off >= 0 ? ti.part_off + ((int64_t)kv * parts + (chained[ui] ? 0 : s)) * n_rows : 0;
           const bool first = s == 0 && !cross_from[ui], last = s + 1 == live && cross_into[ui] < 0;
           w.chain = chained[ui] ? ((first ? 0 : kChainContinues) | (last ? 0 : kChainContinued)) : 0;
           w.pad1 = 0;
@@ -675,7 +677,7 @@ std::string build_plan(const PlanInput& in, Plan* P) {
         const TileInfo& ti = P->tiles[u.tile_off + tl];
         c.p[x] = ti.part_off + (int64_t)(tok - u.tok_begin - uw[us[x]].tile_tok[tl]) * G;
         c.live[x] = ti.live;
-        c.bm[x] = u.bm;
+        c.stride[x] = (uw[us[x]].tile_tok[tl + 1] - uw[us[x]].tile_tok[tl]) * G;
         n += ti.live;
         if (ti.live > 0 && u.bm != kNarrowRows) narrow_only = false;
       }

@@ -65,7 +65,8 @@ struct BranchDesc {
 struct TileInfo {
   int32_t live;        // partials per row from this tile: its live shards, 1 when they form a chain,
                        // 0 when its chain continues into the suffix unit
-  int64_t part_off;    // first partial row (-1: none); row layout ((kv * live + s) * bm + r_in_tile)
+  int64_t part_off;    // first partial row (-1: none); row layout ((kv * live + s) * rows + r_in_tile),
+                       // rows = the tile's rows
 };
 
 struct WorkItem {
@@ -106,13 +107,15 @@ struct TokRec {
 // Where the partials of a token's rows are, for a token whose rows have two
 // or more: for its group-prefix unit (0) and its private-suffix unit (1),
 // row (tok, g) of KV head kv has shard s at workspace row
-// p[x] + (kv * live[x] + s) * bm[x] + g. The rows are combined in the narrow
+// p[x] + (kv * live[x] + s) * stride[x] + g, stride being the rows of the
+// token's M-tile in that unit (a tile's partials are packed: a decode
+// token's 8 rows take 8 workspace rows per shard, not the kernel's 32). The rows are combined in the narrow
 // launch when need > 0 (the number of narrow items per KV head that write
 // them; the last to finish combines), otherwise by the merge kernel.
 struct CombTok {
   int64_t p[2];
   int32_t live[2];
-  int32_t bm[2];
+  int32_t stride[2];
   int32_t need;
   int32_t slot;        // need > 0: the token's arrival counters, one per KV head, are
                        // counters[(slot * H_kv + kv) * kCounterStride]; -1 otherwise

@@ -213,7 +213,7 @@ void check_plan(const std::string& name, const PlanInput& in, const Plan& P) {
         expect(c.need == 0 || c.need == n, name + ": arrivals awaited");
         for (int x = 0; x < 2; ++x)
           if (c.live[x] > 0)
-            expect(c.p[x] >= 0 && c.p[x] + ((int64_t)(in.H_kv - 1) * c.live[x] + c.live[x] - 1) * c.bm[x] + G <= P.part_rows,
+            expect(c.p[x] >= 0 && c.p[x] + ((int64_t)(in.H_kv - 1) * c.live[x] + c.live[x] - 1) * c.stride[x] + G <= P.part_rows,
                    name + ": combination rows inside the workspace");
       }
     }
