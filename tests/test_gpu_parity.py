@@ -158,6 +158,48 @@ def test_random_configurations(seed):
     H.full_parity(w)
 
 
+def _random_decode_workload(seed):
+    """A seeded random decode-class configuration: many branches of one to
+    four new tokens over shared and paged contexts, any G (odd ones too, so
+    that a wave's rows belong to different tokens), d 64 or 128, and shard
+    counts up to 40 -- the tokens whose partials all come from the 32-row
+    kernel are combined inside its launch by the last item to finish."""
+    import random
+    r = random.Random(seed)
+    dtype = "fp32" if r.random() < 0.2 else "bf16"
+    H_kv = r.choice([1, 2, 4, 8])
+    G = r.choice([1, 2, 3, 5, 8])
+    d = r.choice([64, 128])
+    ps = r.choice([1, 8, 16])
+    n_groups = r.choice([1, 2])
+    shared = tuple(r.choice([0, r.randint(100, 3000)]) for _ in range(n_groups))
+    branches = []
+    for g in range(n_groups):
+        for _ in range(r.randint(1, 6)):
+            priv = r.choice([0, r.randint(1, 2000)])
+            if shared[g] + priv == 0:
+                priv = r.randint(1, 500)
+            branches.append((g, min(r.choice([1, 1, 1, 2, 4]), shared[g] + priv), priv))
+    splits = None
+    if r.random() < 0.7:
+        splits = [r.randint(1, 40) for _ in range(n_groups + len(branches))]
+    return custom(f"random_decode_{seed}", dtype=dtype, H_q=H_kv * G, H_kv=H_kv, d=d, page_size=ps,
+                  shared=shared, branches=tuple(branches), causal=r.random() < 0.5, seed=2000 + seed,
+                  splits=splits)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode_configurations(seed):
+    """Seeded random decode-class shapes (the in-launch combination with
+    partial counts up to 40 per unit, from one or two units, rows of several
+    tokens per item), every output against the oracle."""
+    w = _random_decode_workload(seed)
+    H.say(f"  {w.name}: {w.dtype} H_q {w.num_q_heads} H_kv {w.num_kv_heads} d {w.head_dim} ps {w.page_size} "
+          f"groups {[g.shared_len for g in w.groups]} branches {[(b.group, b.q_len, b.private_len) for b in w.branches]} "
+          f"causal {w.causal} splits {w.splits}")
+    H.full_parity(w)
+
+
 @pytest.mark.parametrize("splits", [[4, 2, 1, 3], [1, 1, 1, 1], [16, 5, 4, 9]])
 def test_split_override(splits):
     w = SMALL["fanout_bf16_d128"]()
