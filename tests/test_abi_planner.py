@@ -268,6 +268,18 @@ def test_merge_launch_only_when_wide_partials(name, rows, launch):
         assert stats["workspace_bytes"] == 0
 
 
+def test_partials_packed_at_the_tile_rows():
+    """A tile's partial rows are laid out at the tile's own row count: the 8k
+    decode (one token, G = 8, 32 shards of 8 KV heads) needs 8 rows per
+    (KV head, shard), not the 32-row kernel's full M-tile -- (m, l) as two
+    floats then d fp32 values per row."""
+    w = get_workload("decode_8k")
+    _, _, stats = _plan(w)
+    rows = w.num_kv_heads * 32 * w.group_size
+    ml = -(-rows * 8 // 256) * 256
+    assert stats["workspace_bytes"] == ml + rows * w.head_dim * 4
+
+
 @pytest.mark.parametrize("name,chains", [("prefill_32k", True), ("join_8000_32k", True), ("fanout_8x20_32k", False),
                                          ("join_400_32k", False)])
 def test_shards_of_an_m_tile_chain_when_work_is_plentiful(name, chains):
