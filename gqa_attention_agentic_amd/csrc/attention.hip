@@ -1026,16 +1026,18 @@ __device__ __forceinline__ DmaLane<C> dma_lane(int wave, int lane) {
 // later). Paged sources with power-of-two pages of >= 16 tokens read the
 // tile's page ids with scalar loads, so no vector-memory wait is needed
 // before the addresses are formed.
-template <class C, int D, bool PAGED, bool SCALAR_PAGES, int WHICH>
+// With PRE, the ids of pages lp0 .. lp0 + 4 (clamped to the unit's last
+// page) come in `pre` instead, read ahead by the caller (page_ids_ahead).
+template <class C, int D, bool PAGED, bool SCALAR_PAGES, int WHICH, bool PRE = false>
 __device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLane<C>& L, int wave, int key0,
-                                         int key_end, uint32_t Kst, uint32_t Vst) {
+                                         int key_end, uint32_t Kst, uint32_t Vst, const int* pre = nullptr) {
   int pg[5] = {0, 0, 0, 0, 0};
   int lp0 = 0;
   if (PAGED && SCALAR_PAGES) {
     lp0 = key0 >> src.shift;
     const int lp_last = (key_end - 1) >> src.shift;
 #pragma unroll
-    for (int e = 0; e < 5; ++e) pg[e] = src.table[min(lp0 + e, lp_last)];
+    for (int e = 0; e < 5; ++e) pg[e] = PRE ? pre[e] : src.table[min(lp0 + e, lp_last)];
   }
 #pragma unroll
   for (int q = 0; q < C::PER_WAVE; ++q) {
@@ -1058,6 +1060,17 @@ __device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLa
     if (WHICH & 1) dma16(src.kb + off + L.colK[q], Kst + n * 1024);
     if (WHICH & 2) dma16(src.vb + off + L.colV[q], Vst + n * 1024);
   }
+}
+
+// The page ids a tile starting at key0 needs (paged source, power-of-two
+// pages of >= 16 tokens), as a vector load to be consumed one loop step
+// later: lane e < 5 gets the id of logical page (key0 >> shift) + e, clamped
+// to the unit's last page; lanes past 4 repeat lane 4's load. Issued right
+// behind a tile's DMA, it lands with that tile, so the next DMA issue waits
+// on no page-table round trip.
+__device__ __forceinline__ int page_ids_ahead(const KvSrc<uint16_t>& src, int key0, int key_end, int lane) {
+  const int lp0 = key0 >> src.shift, lp_last = (key_end - 1) >> src.shift;
+  return src.table[min(lp0 + min(lane, 4), lp_last)];
 }
 
 template <class C, int D, int WHICH = 3, typename P>
@@ -1429,6 +1442,7 @@ attn_narrow_dma(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char st[C::WAVES * 2 * C::TB];   // per wave: K tile then V tile
   __shared__ float2 mml[C::WAVES * 64];
   __shared__ CombLds<C::BM> cl;
+  __shared__ int pids[C::WAVES * 8];   // per wave: the page ids read ahead, parked during the tile's compute
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i = lane & 31, h = lane >> 5;
   const DmaLane<C> L = dma_lane<C>(0, lane);
   const int bin_begin = a.bins[blockIdx.x], bin_end = a.bins[blockIdx.x + 1];
@@ -1449,19 +1463,35 @@ attn_narrow_dma(AttnArgs a) {
     State<C> s;
     load_q<C, uint16_t, D>(a, w, it.kv, h, s);
     if (wave < nt) dma_tile_any<C, D>(src, L, 0, kb0 + wave * C::BN, ke, K0, V0);
+    // Paged K/V: the page ids of the wave's next tile are read one step
+    // ahead (page_ids_ahead), so its DMA can go out as soon as this tile's
+    // stage is consumed.
+    const bool ahead = src.paged && src.shift >= 4;
+    int ids = 0;
+    if (ahead && wave + C::WAVES < nt) ids = page_ids_ahead(src, kb0 + (wave + C::WAVES) * C::BN, ke, lane);
     combine_prepare(a, it, wave, lane, &cl);
-    const RowDest dst = row_dest(a, it, w, i);
     int pmin, pmax;
     wave_pos_range(w, &pmin, &pmax);
     const bool active = it.n_rows > 0;
     const float c = a.scale_log2;
     for (int j = wave; j < nt; j += C::WAVES) {
-      wait_dma<0>();
+      wait_dma<0>();   // this tile, and the page ids of the next one
+      if (ahead && lane < 8) pids[wave * 8 + lane] = ids;
       dma_step<C, D>(lds_u32(K0), lds_u32(V0), L, s, it.key_pos0, kb0 + j * C::BN, ke, causal, w.pos, pmin, pmax,
                      active, c, i, h);
       if (j + C::WAVES < nt) {
         wait_dma<63>();   // own LDS reads of the stage done
-        dma_tile_any<C, D>(src, L, 0, kb0 + (j + C::WAVES) * C::BN, ke, K0, V0);
+        const int key0n = kb0 + (j + C::WAVES) * C::BN;
+        if (ahead) {
+          const int parked = pids[wave * 8 + min(lane, 4)];
+          int pg[5];
+#pragma unroll
+          for (int e = 0; e < 5; ++e) pg[e] = __builtin_amdgcn_readlane(parked, e);
+          dma_tile<C, D, true, true, 3, true>(src, L, 0, key0n, ke, lds_u32(K0), lds_u32(V0), pg);
+          if (j + 2 * C::WAVES < nt) ids = page_ids_ahead(src, key0n + C::WAVES * C::BN, ke, lane);
+        } else {
+          dma_tile_any<C, D>(src, L, 0, key0n, ke, K0, V0);
+        }
       }
     }
     // Merge the eight waves' states (same rows, disjoint keys) through LDS:
@@ -1469,6 +1499,12 @@ attn_narrow_dma(AttnArgs a) {
     // tile's 32), four accumulator entries per LDS access, and every wave
     // combines a quarter or half of one O^T block.
     s.l += __shfl_xor(s.l, 32);
+    const RowDest dst = row_dest(a, it, w, i);
+    // Addresses of this phase come from an opaque copy of the lane index, so
+    // the compiler forms them here instead of hoisting them out of the item
+    // loop, where they would hold registers through the K/V stream.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     wait_dma<0>();
     __syncthreads();
     float4* mo = (float4*)st;                     // [wave][db][group of 4 entries][lane]
@@ -1477,10 +1513,10 @@ attn_narrow_dma(AttnArgs a) {
       for (int db = 0; db < C::OB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          mo[((wave * C::OB + db) * 4 + r4) * 64 + lane] =
+          mo[((wave * C::OB + db) * 4 + r4) * 64 + ln] =
               make_float4(s.o[db][4 * r4], s.o[db][4 * r4 + 1], s.o[db][4 * r4 + 2], s.o[db][4 * r4 + 3]);
     }
-    mml[wave * 64 + lane] = make_float2(s.m, s.l);
+    mml[wave * 64 + ln] = make_float2(s.m, s.l);
     __syncthreads();
     {
       constexpr int WPB = C::WAVES / C::OB, NQ = 4 / WPB;   // waves per O^T block, entry groups per wave
@@ -1489,7 +1525,7 @@ attn_narrow_dma(AttnArgs a) {
       float M = kNegInf;
 #pragma unroll
       for (int k = 0; k < C::WAVES; ++k) {
-        const float2 x = mml[k * 64 + lane];
+        const float2 x = mml[k * 64 + ln];
         mk[k] = x.x;
         lk[k] = x.y;
         M = fmaxf(M, x.x);
@@ -1508,7 +1544,7 @@ attn_narrow_dma(AttnArgs a) {
         if (!w.ok) continue;
 #pragma unroll
         for (int k = 0; k < C::WAVES; ++k) {
-          const float4 v = mo[((k * C::OB + db) * 4 + q0 + j) * 64 + lane];
+          const float4 v = mo[((k * C::OB + db) * 4 + q0 + j) * 64 + ln];
           acc[j].x += wk[k] * v.x;
           acc[j].y += wk[k] * v.y;
           acc[j].z += wk[k] * v.z;
