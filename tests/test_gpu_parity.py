@@ -92,6 +92,14 @@ SMALL = {
     "decodes_several_items_per_workgroup": lambda: custom(
         "decodes_several_items_per_workgroup", shared=(0,), branches=tuple((0, 1, 1500 + 37 * k) for k in range(48)),
         seed=127, splits=[0] + [4] * 48),
+    # Long paged items in the narrow kernel (few shards, a dozen or more
+    # tiles per wave), so each wave's next page ids are read a tile ahead,
+    # over pages of 32 and 64 tokens with ragged last pages.
+    "paged_decode_long_items_page32": lambda: custom("paged_decode_long_items_page32", page_size=32, shared=(0,),
+                                                     branches=((0, 1, 6001),), seed=141, splits=[0, 2]),
+    "paged_decode_long_items_d64_page64": lambda: custom("paged_decode_long_items_d64_page64", d=64, page_size=64,
+                                                         shared=(0,), branches=((0, 1, 4099), (0, 1, 2500)),
+                                                         seed=143, splits=[0, 1, 1]),
     # Decode-shaped tokens combined inside the narrow launch, past the fold's
     # first 64 partials (d = 128: one row per wave; d = 64: two rows per
     # wave), and with partials from both a prefix and a suffix unit.
