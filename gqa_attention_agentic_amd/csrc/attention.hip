@@ -1023,11 +1023,11 @@ __device__ __forceinline__ DmaLane<C> dma_lane(int wave, int lane) {
 
 // Issue the DMA of tile `t` (unit-local first key key0) into one ring stage.
 // Keys past key_end are clamped to the last valid key (finite data, masked
-// later). Paged sources with power-of-two pages of >= 16 tokens read the
-// tile's page ids with scalar loads, so no vector-memory wait is needed
-// before the addresses are formed.
-// With PRE, the ids of pages lp0 .. lp0 + 4 (clamped to the unit's last
-// page) come in `pre` instead, read ahead by the caller (page_ids_ahead).
+// later). Paged sources with power-of-two pages of >= 16 tokens look up the
+// ids of the at most five pages the tile touches, not one id per key; those
+// lookups are loads the DMA addresses wait for. With PRE, the ids of pages
+// lp0 .. lp0 + 4 (clamped to the unit's last page) come in `pre` instead,
+// read ahead by the caller (page_ids_ahead).
 template <class C, int D, bool PAGED, bool SCALAR_PAGES, int WHICH, bool PRE = false>
 __device__ __forceinline__ void dma_tile(const KvSrc<uint16_t>& src, const DmaLane<C>& L, int wave, int key0,
                                          int key_end, uint32_t Kst, uint32_t Vst, const int* pre = nullptr) {
