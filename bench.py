@@ -677,7 +677,7 @@ def main():
                          "under a profiler can be scaled by a copy of known size")
     ap.add_argument("--sweep-splits", choices=sorted(SWEEPS), default=None,
                     help="time the workload over a range of split counts instead of the bench line")
-    ap.add_argument("--sweep-out", default="gpurun_out/sweep.json")
+    ap.add_argument("--sweep-out", default="sweep.json")
     ap.add_argument("--trace-summary", nargs=2, metavar=("SWEEP_JSON", "KERNEL_TRACE_CSV"), default=None,
                     help="print per-point rocprofv3 kernel durations of a sweep run (no GPU needed)")
     ap.add_argument("--kernel-summary", metavar="KERNEL_TRACE_CSV", default=None,
